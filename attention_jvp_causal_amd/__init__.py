@@ -1,0 +1,241 @@
+"""MI355X (gfx950) custom-mask attention JVP: Python binding of the C ABI.
+
+The work is done by hand-written HIP kernels in ``libattnjvp.so`` (built
+in-tree by ``attention_jvp_causal_amd.build``).  This module only marshals
+arguments: it checks tensors, allocates outputs with torch (device memory and
+streams are torch's), and calls the C entry points declared in
+``include/attn_jvp.h`` through ctypes.  There is no fallback: if the library is
+missing, every call raises.
+
+    desc = attn_jvp_mask_desc_build("block_causal", num_frames=21, frame_tokens=1560,
+                                    frames_per_chunk=3, head_dim=128, dtype="bf16")
+    o, to, lse = attn_jvp_fwd(q, k, v, tq, tk, tv, desc)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattnjvp.so")
+
+AJ_OK, AJ_EINVAL, AJ_ENOTSUP, AJ_ENOMEM, AJ_EHIP, AJ_EMASK = range(6)
+AJ_F32, AJ_BF16 = 0, 1
+MASK_KINDS = {"full": 0, "block_causal": 1, "frame_causal": 1, "tf_clean_noisy": 2}
+DTYPES = {"f32": AJ_F32, "float32": AJ_F32, "bf16": AJ_BF16, "bfloat16": AJ_BF16}
+
+
+class AttnJvpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+class aj_mask_spec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_frames", ctypes.c_int32),
+                ("frame_tokens", ctypes.c_int32), ("frames_per_chunk", ctypes.c_int32)]
+
+
+class aj_mask_stats(ctypes.Structure):
+    _fields_ = [("unmasked_pairs", ctypes.c_int64), ("seq_len", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("num_q_tiles", ctypes.c_int32), ("num_k_tiles", ctypes.c_int32),
+                ("full_tiles", ctypes.c_int32), ("partial_tiles", ctypes.c_int32),
+                ("num_entries", ctypes.c_int32)]
+
+
+class aj_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("in_stride_b", ctypes.c_int64), ("in_stride_h", ctypes.c_int64), ("in_stride_l", ctypes.c_int64),
+                ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_l", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_jvp_causal_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    pdesc = ctypes.c_void_p
+    L.attn_jvp_status_str.argtypes, L.attn_jvp_status_str.restype = [i32], ctypes.c_char_p
+    L.attn_jvp_version.argtypes, L.attn_jvp_version.restype = [], i32
+    L.attn_jvp_mask_desc_build.argtypes = [ctypes.POINTER(aj_mask_spec), i32, i32, i32, ctypes.POINTER(pdesc)]
+    L.attn_jvp_mask_desc_from_rects.argtypes = [i32, P, i32, i32, i32, ctypes.POINTER(pdesc)]
+    L.attn_jvp_mask_desc_stats.argtypes = [pdesc, ctypes.POINTER(aj_mask_stats)]
+    L.attn_jvp_mask_desc_tile_kind.argtypes = [pdesc, i32, i32, ctypes.POINTER(i32)]
+    L.attn_jvp_mask_desc_row_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
+    L.attn_jvp_mask_desc_free.argtypes, L.attn_jvp_mask_desc_free.restype = [pdesc], None
+    L.attn_jvp_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
+    for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
+               "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd"):
+        getattr(L, fn).restype = i32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().attn_jvp_status_str(int(status)).decode()
+
+
+def attn_jvp_version() -> int:
+    return int(lib().attn_jvp_version())
+
+
+def _check(st: int, where: str) -> None:
+    if st != AJ_OK:
+        raise AttnJvpError(st, where)
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    key = str(dtype).replace("torch.", "")
+    if key not in DTYPES:
+        raise ValueError(f"unsupported dtype {dtype!r}")
+    return DTYPES[key]
+
+
+class MaskDesc:
+    """Owner of an ``aj_mask_desc*`` (freed on close / garbage collection)."""
+
+    def __init__(self, handle: int, head_dim: int, dtype: int):
+        self._h = ctypes.c_void_p(handle)
+        self.head_dim = head_dim
+        self.dtype = dtype
+        s = self.stats()
+        self.seq_len = s["seq_len"]
+        self.unmasked_pairs = s["unmasked_pairs"]
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("mask descriptor already freed")
+        return self._h
+
+    def stats(self) -> dict:
+        st = aj_mask_stats()
+        _check(lib().attn_jvp_mask_desc_stats(self.handle, ctypes.byref(st)), "attn_jvp_mask_desc_stats")
+        return {f: getattr(st, f) for f, _ in aj_mask_stats._fields_}
+
+    def tile_kind(self, q_tile: int, k_tile: int) -> int:
+        k = ctypes.c_int32()
+        _check(lib().attn_jvp_mask_desc_tile_kind(self.handle, q_tile, k_tile, ctypes.byref(k)),
+               "attn_jvp_mask_desc_tile_kind")
+        return k.value
+
+    def row_bits(self, q_tile: int, k_tile: int, row: int) -> int:
+        b = ctypes.c_uint64()
+        _check(lib().attn_jvp_mask_desc_row_bits(self.handle, q_tile, k_tile, row, ctypes.byref(b)),
+               "attn_jvp_mask_desc_row_bits")
+        return b.value
+
+    def close(self) -> None:
+        if self._h:
+            attn_jvp_mask_desc_free(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def attn_jvp_mask_desc_build(kind: str, num_frames: int, frame_tokens: int, frames_per_chunk: int = 1,
+                             head_dim: int = 128, dtype="bf16", seq_len: Optional[int] = None) -> MaskDesc:
+    """Descriptor for a frame-level layout (see ``aj_mask_kind`` in the header)."""
+    k = MASK_KINDS[kind] if isinstance(kind, str) else int(kind)
+    spec = aj_mask_spec(k, num_frames, frame_tokens, frames_per_chunk)
+    if seq_len is None:
+        seq_len = num_frames * frame_tokens * (2 if k == MASK_KINDS["tf_clean_noisy"] else 1)
+    out = ctypes.c_void_p()
+    dt = _dtype_code(dtype)
+    _check(lib().attn_jvp_mask_desc_build(ctypes.byref(spec), seq_len, head_dim, dt, ctypes.byref(out)),
+           "attn_jvp_mask_desc_build")
+    return MaskDesc(out.value, head_dim, dt)
+
+
+def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], head_dim: int = 128,
+                                  dtype="bf16") -> MaskDesc:
+    """Descriptor from disjoint half-open rectangles (q0, q1, k0, k1)."""
+    flat = [int(x) for r in rects for x in r]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    out = ctypes.c_void_p()
+    dt = _dtype_code(dtype)
+    _check(lib().attn_jvp_mask_desc_from_rects(seq_len, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 4,
+                                               head_dim, dt, ctypes.byref(out)),
+           "attn_jvp_mask_desc_from_rects")
+    return MaskDesc(out.value, head_dim, dt)
+
+
+def attn_jvp_mask_desc_free(handle) -> None:
+    lib().attn_jvp_mask_desc_free(handle)
+
+
+def attn_jvp_fwd(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = None,
+                 out_dtype=None, out: Optional[Tuple] = None, stream=None):
+    """O, tO, lse of masked attention and its JVP on the GPU (one kernel launch).
+
+    q, k, v, tq, tk, tv: CUDA/HIP tensors [B, H, L, D] (bf16 or fp32) with the
+    D axis contiguous and identical strides.  Returns (o, to, lse): o and to
+    [B, H, L, D] in ``out_dtype`` (default: the input dtype), lse [B, H, L]
+    float32.  ``out`` may pass preallocated (o, to, lse).
+    """
+    import torch
+
+    ins = (q, k, v, tq, tk, tv)
+    x0 = q
+    if any(t.device != x0.device for t in ins) or x0.device.type != "cuda":
+        raise ValueError("all inputs must be on the same GPU device")
+    if any(t.dtype != x0.dtype for t in ins) or any(t.shape != x0.shape for t in ins):
+        raise ValueError("inputs must share dtype and shape")
+    if any(t.stride() != x0.stride() for t in ins):
+        raise ValueError("inputs must share strides")
+    if x0.dim() != 4 or x0.stride(3) != 1:
+        raise ValueError("inputs must be [B, H, L, D] with D contiguous")
+    B, H, L, D = x0.shape
+    in_dt = {torch.bfloat16: AJ_BF16, torch.float32: AJ_F32}.get(x0.dtype)
+    if in_dt is None:
+        raise ValueError(f"unsupported input dtype {x0.dtype}")
+    odt = x0.dtype if out_dtype is None else out_dtype
+    out_dt = {torch.bfloat16: AJ_BF16, torch.float32: AJ_F32}.get(odt)
+    if out_dt is None:
+        raise ValueError(f"unsupported output dtype {odt}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        o = torch.empty((B, H, L, D), dtype=odt, device=x0.device)
+        to = torch.empty_like(o)
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=x0.device)
+    else:
+        o, to, lse = out
+        if o.shape != x0.shape or to.shape != x0.shape or o.dtype != odt or to.dtype != odt:
+            raise ValueError("preallocated o / to have the wrong shape or dtype")
+        if o.stride() != to.stride() or o.stride(3) != 1:
+            raise ValueError("preallocated o / to must share strides with D contiguous")
+        if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("preallocated lse must be a contiguous float32 [B, H, L] tensor")
+    sh = aj_shape(B, H, L, D, in_dt, out_dt, *x0.stride()[:3], *o.stride()[:3])
+    if stream is None:
+        stream = torch.cuda.current_stream(x0.device).cuda_stream
+    with torch.cuda.device(x0.device):
+        st = lib().attn_jvp_fwd(ctypes.byref(sh), *(t.data_ptr() for t in ins), mask.handle, float(scale),
+                                o.data_ptr(), to.data_ptr(), lse.data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_jvp_fwd")
+    return o, to, lse
+
+
+__all__ = [
+    "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_F32", "AJ_BF16",
+    "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
+    "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_free", "attn_jvp_fwd", "LIB_PATH",
+]

@@ -1,0 +1,62 @@
+// Internal definitions shared by the host side of the attention-JVP library:
+// the mask descriptor (tile map built from admissible rectangles) and the
+// kernel launch arguments.  Not part of the public C ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/attn_jvp.h"
+
+namespace aj {
+
+// Tile geometry of the kernels.  Every instantiation (bf16 / fp32, D = 64 / 128)
+// uses 128 query rows per workgroup (4 waves x 32 rows) and 64 keys per
+// streamed tile, so one key bitmask row is one 64-bit word.
+constexpr int kTileM = 128;
+constexpr int kTileN = 64;
+constexpr int kMaxDevices = 64;
+
+inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
+inline bool supported_dtype(int t) { return t == AJ_F32 || t == AJ_BF16; }
+
+// One run of key tiles visited by a query tile.  pidx < 0: every tile in
+// [kt0, kt1) is full.  pidx >= 0: the single tile kt0 (kt1 = kt0 + 1) is
+// partial and its per-row key bitmask starts at bits[pidx * kTileM].
+struct Entry {
+  int32_t kt0, kt1, pidx, pad;
+};
+
+struct DeviceTables {
+  void* base = nullptr;         // one hipMalloc holding everything below
+  const int32_t* qt_off = nullptr;
+  const Entry* entries = nullptr;
+  const int32_t* tasks = nullptr;
+  const uint64_t* bits = nullptr;
+};
+
+}  // namespace aj
+
+struct aj_mask_desc {
+  int32_t seq_len = 0, head_dim = 0, dtype = 0;
+  int32_t tile_m = aj::kTileM, tile_n = aj::kTileN;
+  int32_t n_qt = 0, n_kt = 0;
+  int64_t pairs = 0;
+  int32_t full_tiles = 0, partial_tiles = 0;
+  std::vector<int32_t> qt_off;      // n_qt + 1 offsets into entries
+  std::vector<aj::Entry> entries;
+  std::vector<int32_t> tasks;       // query tiles, most key tiles first
+  std::vector<uint64_t> bits;       // partial_tiles * tile_m words
+  std::mutex mu;                    // guards dev[]
+  aj::DeviceTables dev[aj::kMaxDevices];
+};
+
+namespace aj {
+// Builds the tile map from validated, disjoint rectangles {q0,q1,k0,k1}.
+int32_t build_from_rects(int32_t seq_len, const int32_t* rects, int32_t n, int32_t head_dim,
+                         int32_t dtype, aj_mask_desc** out);
+// Expands a frame-level layout into disjoint rectangles.
+int32_t layout_rects(const aj_mask_spec* spec, int32_t seq_len, std::vector<int32_t>* rects);
+}  // namespace aj

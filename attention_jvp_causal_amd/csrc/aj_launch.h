@@ -1,0 +1,36 @@
+// Kernel launch arguments and the launcher shared by the C ABI and the HIP
+// kernels.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aj_internal.h"
+
+namespace aj {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* tq;
+  const void* tk;
+  const void* tv;
+  void* o;
+  void* to;
+  float* lse;
+  int64_t isb, ish, isl;  // input strides (elements)
+  int64_t osb, osh, osl;  // output strides (elements)
+  int32_t B, H, L, n_tasks;
+  float scale;       // softmax scale c
+  float scale_log2;  // c * log2(e)
+  const int32_t* qt_off;
+  const Entry* entries;
+  const int32_t* tasks;
+  const uint64_t* bits;
+};
+
+// Enqueues the forward kernel; returns an aj_status.
+int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, hipStream_t stream);
+
+}  // namespace aj

@@ -1,0 +1,216 @@
+// C ABI of the attention-JVP library: argument validation, mask descriptor
+// lifetime and device upload, and kernel dispatch.  See include/attn_jvp.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "aj_internal.h"
+#include "aj_launch.h"
+
+using aj::DeviceTables;
+using aj::Entry;
+
+namespace {
+
+constexpr int32_t kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Uploads the descriptor's tables to the current device once; returns the
+// device copy or an error status.
+int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
+  aj_mask_desc* d = const_cast<aj_mask_desc*>(cd);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AJ_EHIP;
+  if (dev < 0 || dev >= aj::kMaxDevices) return AJ_ENOTSUP;
+  std::lock_guard<std::mutex> lock(d->mu);
+  DeviceTables& t = d->dev[dev];
+  if (t.base) {
+    *out = &t;
+    return AJ_OK;
+  }
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t n_off = d->qt_off.size() * sizeof(int32_t);
+  const size_t n_ent = std::max<size_t>(1, d->entries.size()) * sizeof(Entry);
+  const size_t n_task = d->tasks.size() * sizeof(int32_t);
+  const size_t n_bits = std::max<size_t>(1, d->bits.size()) * sizeof(uint64_t);
+  const size_t o_ent = align(n_off), o_task = o_ent + align(n_ent), o_bits = o_task + align(n_task);
+  const size_t total = o_bits + align(n_bits);
+  std::vector<uint8_t> host(total, 0);
+  std::memcpy(host.data(), d->qt_off.data(), n_off);
+  if (!d->entries.empty()) std::memcpy(host.data() + o_ent, d->entries.data(), d->entries.size() * sizeof(Entry));
+  std::memcpy(host.data() + o_task, d->tasks.data(), n_task);
+  if (!d->bits.empty()) std::memcpy(host.data() + o_bits, d->bits.data(), d->bits.size() * sizeof(uint64_t));
+  void* base = nullptr;
+  if (hipMalloc(&base, total) != hipSuccess) return AJ_ENOMEM;
+  if (hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(base);
+    return AJ_EHIP;
+  }
+  uint8_t* b = static_cast<uint8_t*>(base);
+  t.qt_off = reinterpret_cast<const int32_t*>(b);
+  t.entries = reinterpret_cast<const Entry*>(b + o_ent);
+  t.tasks = reinterpret_cast<const int32_t*>(b + o_task);
+  t.bits = reinterpret_cast<const uint64_t*>(b + o_bits);
+  t.base = base;
+  *out = &t;
+  return AJ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_jvp_status_str(int32_t status) {
+  switch (status) {
+    case AJ_OK: return "AJ_OK: success";
+    case AJ_EINVAL: return "AJ_EINVAL: invalid argument";
+    case AJ_ENOTSUP: return "AJ_ENOTSUP: unsupported head_dim or dtype";
+    case AJ_ENOMEM: return "AJ_ENOMEM: allocation failed";
+    case AJ_EHIP: return "AJ_EHIP: HIP runtime error";
+    case AJ_EMASK: return "AJ_EMASK: invalid mask or descriptor mismatch";
+    default: return "unknown status";
+  }
+}
+
+int32_t attn_jvp_version(void) { return kVersion; }
+
+int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int32_t head_dim,
+                                 int32_t dtype, aj_mask_desc** out) {
+  if (!out) return AJ_EINVAL;
+  *out = nullptr;
+  if (!spec || seq_len < 1) return AJ_EINVAL;
+  if (!aj::supported_head_dim(head_dim) || !aj::supported_dtype(dtype)) return AJ_ENOTSUP;
+  try {
+    std::vector<int32_t> rects;
+    const int32_t st = aj::layout_rects(spec, seq_len, &rects);
+    if (st != AJ_OK) return st;
+    return aj::build_from_rects(seq_len, rects.data(), int32_t(rects.size() / 4), head_dim, dtype, out);
+  } catch (const std::bad_alloc&) {
+    return AJ_ENOMEM;
+  } catch (...) {
+    return AJ_EINVAL;
+  }
+}
+
+int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
+                                      int32_t head_dim, int32_t dtype, aj_mask_desc** out) {
+  return aj::build_from_rects(seq_len, rects, n_rects, head_dim, dtype, out);
+}
+
+int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* d, aj_mask_stats* s) {
+  if (!d || !s) return AJ_EINVAL;
+  s->unmasked_pairs = d->pairs;
+  s->seq_len = d->seq_len;
+  s->tile_m = d->tile_m;
+  s->tile_n = d->tile_n;
+  s->num_q_tiles = d->n_qt;
+  s->num_k_tiles = d->n_kt;
+  s->full_tiles = d->full_tiles;
+  s->partial_tiles = d->partial_tiles;
+  s->num_entries = int32_t(d->entries.size());
+  return AJ_OK;
+}
+
+static const Entry* find_entry(const aj_mask_desc* d, int32_t qt, int32_t kt) {
+  for (int32_t e = d->qt_off[qt]; e < d->qt_off[qt + 1]; ++e)
+    if (d->entries[e].kt0 <= kt && kt < d->entries[e].kt1) return &d->entries[e];
+  return nullptr;
+}
+
+int32_t attn_jvp_mask_desc_tile_kind(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t* kind) {
+  if (!d || !kind || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt) return AJ_EINVAL;
+  const Entry* e = find_entry(d, qt, kt);
+  *kind = !e ? 0 : (e->pidx >= 0 ? 1 : 2);
+  return AJ_OK;
+}
+
+int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t row,
+                                    uint64_t* bits) {
+  if (!d || !bits || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt || row < 0 || row >= d->tile_m)
+    return AJ_EINVAL;
+  const Entry* e = find_entry(d, qt, kt);
+  if (!e || qt * d->tile_m + row >= d->seq_len) *bits = 0;
+  else if (e->pidx < 0) *bits = ~0ull;
+  else *bits = d->bits[size_t(e->pidx) * d->tile_m + row];
+  return AJ_OK;
+}
+
+void attn_jvp_mask_desc_free(aj_mask_desc* d) {
+  if (!d) return;
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < aj::kMaxDevices; ++dev) {
+    if (!d->dev[dev].base) continue;
+    if (hipSetDevice(dev) == hipSuccess) (void)hipFree(d->dev[dev].base);
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+  delete d;
+}
+
+int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq,
+                     const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
+                     void* to, float* lse, void* stream) {
+  if (!s || !mask) return AJ_EINVAL;
+  const void* ins[6] = {q, k, v, tq, tk, tv};
+  const void* outs[3] = {o, to, lse};
+  for (const void* p : ins)
+    if (!p || !aligned16(p)) return AJ_EINVAL;
+  for (const void* p : outs)
+    if (!p || !aligned16(p)) return AJ_EINVAL;
+  if (s->batch < 1 || s->heads < 1 || s->seq_len < 1) return AJ_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return AJ_EINVAL;
+  if (!aj::supported_head_dim(s->head_dim)) return AJ_ENOTSUP;
+  if (!aj::supported_dtype(s->in_dtype) || !aj::supported_dtype(s->out_dtype)) return AJ_ENOTSUP;
+  if (s->in_dtype == AJ_F32 && s->out_dtype != AJ_F32) return AJ_ENOTSUP;
+  const int64_t esz_in = s->in_dtype == AJ_F32 ? 4 : 2, esz_out = s->out_dtype == AJ_F32 ? 4 : 2;
+  const int64_t vin = 16 / esz_in, vout = 16 / esz_out;  // elements per 16 bytes
+  const int64_t D = s->head_dim, L = s->seq_len;
+  // strides: non-negative, 16-byte multiples, rows at least D apart
+  const int64_t is[3] = {s->in_stride_b, s->in_stride_h, s->in_stride_l};
+  const int64_t os[3] = {s->out_stride_b, s->out_stride_h, s->out_stride_l};
+  for (int i = 0; i < 3; ++i) {
+    if (is[i] < 0 || is[i] % vin != 0 || os[i] < 0 || os[i] % vout != 0) return AJ_EINVAL;
+  }
+  // outputs must not overlap themselves: sorted by stride, every stride must
+  // clear the extent of the axes below it (rows are D elements long).  Inputs
+  // are only read and may alias (a zero stride broadcasts).
+  {
+    int64_t st3[3][2] = {{os[0], s->batch}, {os[1], s->heads}, {os[2], L}};
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (st3[j][0] < st3[i][0]) std::swap(st3[i], st3[j]);
+    int64_t span = D;
+    for (int i = 0; i < 3; ++i) {
+      if (st3[i][1] == 1) continue;
+      if (st3[i][0] < span) return AJ_EINVAL;
+      span = st3[i][0] * st3[i][1];
+    }
+  }
+  if (mask->seq_len != s->seq_len || mask->head_dim != s->head_dim || mask->dtype != s->in_dtype)
+    return AJ_EMASK;
+  const int64_t BHL = int64_t(s->batch) * s->heads * L;
+  if (BHL > (int64_t(1) << 40)) return AJ_EINVAL;
+
+  const DeviceTables* t = nullptr;
+  int32_t st = device_tables(mask, &t);
+  if (st != AJ_OK) return st;
+
+  aj::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv;
+  a.o = o; a.to = to; a.lse = lse;
+  a.isb = s->in_stride_b; a.ish = s->in_stride_h; a.isl = s->in_stride_l;
+  a.osb = s->out_stride_b; a.osh = s->out_stride_h; a.osl = s->out_stride_l;
+  a.B = s->batch; a.H = s->heads; a.L = s->seq_len;
+  a.n_tasks = mask->n_qt;
+  a.scale = scale;
+  a.scale_log2 = float(double(scale) * 1.4426950408889634074);
+  a.qt_off = t->qt_off; a.entries = t->entries; a.tasks = t->tasks; a.bits = t->bits;
+  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

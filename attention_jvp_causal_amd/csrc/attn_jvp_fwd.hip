@@ -1,0 +1,528 @@
+// Custom-mask attention JVP forward for gfx950 (MI355X).
+//
+// "Causal-rCM", App. B: one online-softmax pass computes the primal output of
+// masked attention (Eq. 42) and its tangent (Eq. 44, evaluated as Eq. 45),
+// streaming only the admissible key tiles of the mask; the same tile schedule
+// serves the scores and their tangents.
+//
+// Work decomposition.  A workgroup (4 waves, 256 lanes) owns one 128-row query
+// tile of one (batch, head); wave w owns query rows 32w..32w+31 of that tile.
+// Keys stream in tiles of 64 through LDS.  Per key tile and wave:
+//   S^T  = K Q^T             (keys x queries, MFMA 32x32x16 bf16, fp32 acc)
+//   tS^T = tK Q^T + K tQ^T   (one accumulator chain)
+// Computing the transposed scores puts one query row in each lane (lanes l and
+// l+32 share a row and split its keys), so the softmax statistics are per lane
+// and the accumulator registers feed the next MFMA as its B operand without any
+// data movement:
+//   O^T  += V^T  P~^T        A^T += V^T (P~ . tS)^T        B^T += tV^T P~^T
+// V and tV are therefore staged transposed (d-major) in LDS.
+//
+// Online softmax (fp32, per row): running max m, denominator l, and the JVP
+// accumulators A = sum p~ ts v, B = sum p~ tv, mu = sum p~ ts share one rescale
+// factor with O.  Finally O = O~/l and tO = (A + B - mu O)/l (Eq. 45).
+// Rescaling is lazy: the reference max only moves when a row's max grows by
+// more than 2^8, which is exact in real arithmetic (all terms of a row share
+// the reference) and bounds p~ by 256.
+// The bf16 MFMA operands p~ and p~.ts are rounded once; l and mu are summed
+// from the same rounded values, so the cancellation in A - mu O is exact for
+// the rounded operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aj_internal.h"
+#include "aj_launch.h"
+
+namespace aj {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BM = kTileM;   // query rows per workgroup
+constexpr int BN = kTileN;   // keys per streamed tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr float kLazyRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2^8
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// ---------------------------------------------------------------------------
+// bf16 inputs
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct Bf16Lds {
+  static constexpr int KP = D + 8;   // K / tK row pitch (elements): 16-byte rows, conflict-free b128 reads
+  static constexpr int VP = BN + 4;  // V^T / tV^T row pitch: 136 bytes, conflict-free b64 reads
+  uint16_t k[BN * KP];
+  uint16_t tk[BN * KP];
+  uint16_t vt[D * VP];
+  uint16_t tvt[D * VP];
+};
+
+// Global -> LDS staging of one key tile.  K and tK are copied row-major in
+// 16-byte chunks (consecutive lanes read consecutive chunks of a key row).
+// V and tV are transposed on the way: a lane reads 8 values of d for 4
+// consecutive keys and writes 8 four-key runs V^T[d][4g..4g+3].  Keys >= L
+// read as zero.
+template <int D>
+__device__ __forceinline__ void stage_tile_bf16(Bf16Lds<D>& s, const uint16_t* __restrict__ K,
+                                                const uint16_t* __restrict__ tK,
+                                                const uint16_t* __restrict__ V,
+                                                const uint16_t* __restrict__ tV, int64_t sl,
+                                                int key0, int L, int tid) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int NK = BN * CH / NTHREADS;    // K chunks per lane
+  constexpr int NU = (BN / 4) * CH;         // transpose units per tensor
+  constexpr int NV = 2 * NU / NTHREADS;     // units (V and tV) per lane
+  static_assert(NK * NTHREADS == BN * CH, "K staging must tile evenly");
+  static_assert(NV * NTHREADS == 2 * NU, "V staging must tile evenly");
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  u32x4_t kr[NK], tkr[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int key = c / CH, col = (c % CH) * 8;
+    const int gk = key0 + key;
+    kr[i] = gk < L ? *(const u32x4_t*)(K + gk * sl + col) : zero;
+    tkr[i] = gk < L ? *(const u32x4_t*)(tK + gk * sl + col) : zero;
+  }
+  u32x4_t vr[NV][4];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int u = tid + i * NTHREADS;
+    const bool is_t = u >= NU;
+    const int uu = is_t ? u - NU : u;
+    const int g = uu % (BN / 4), col = (uu / (BN / 4)) * 8;
+    const uint16_t* src = is_t ? tV : V;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gk = key0 + 4 * g + j;
+      vr[i][j] = gk < L ? *(const u32x4_t*)(src + gk * sl + col) : zero;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int key = c / CH, col = (c % CH) * 8;
+    *(u32x4_t*)(s.k + key * Bf16Lds<D>::KP + col) = kr[i];
+    *(u32x4_t*)(s.tk + key * Bf16Lds<D>::KP + col) = tkr[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int u = tid + i * NTHREADS;
+    const bool is_t = u >= NU;
+    const int uu = is_t ? u - NU : u;
+    const int g = uu % (BN / 4), col = (uu / (BN / 4)) * 8;
+    uint16_t* dst = (is_t ? s.tvt : s.vt) + col * Bf16Lds<D>::VP + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // dword m of key j's chunk holds d = col+2m (low half) and col+2m+1 (high half)
+      u32x2_t ev, od;
+      ev.x = __builtin_amdgcn_perm(vr[i][1][m], vr[i][0][m], 0x05040100u);
+      ev.y = __builtin_amdgcn_perm(vr[i][3][m], vr[i][2][m], 0x05040100u);
+      od.x = __builtin_amdgcn_perm(vr[i][1][m], vr[i][0][m], 0x07060302u);
+      od.y = __builtin_amdgcn_perm(vr[i][3][m], vr[i][2][m], 0x07060302u);
+      *(u32x2_t*)(dst + (2 * m) * Bf16Lds<D>::VP) = ev;
+      *(u32x2_t*)(dst + (2 * m + 1) * Bf16Lds<D>::VP) = od;
+    }
+  }
+}
+
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
+void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
+  constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
+  using Lds = Bf16Lds<D>;
+  __shared__ __attribute__((aligned(16))) Lds s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int qt = a.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
+  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + in_off;
+  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + in_off;
+  const uint16_t* __restrict__ tQg = (const uint16_t*)a.tq + in_off;
+  const uint16_t* __restrict__ tKg = (const uint16_t*)a.tk + in_off;
+  const uint16_t* __restrict__ tVg = (const uint16_t*)a.tv + in_off;
+  const int q_row = qt * BM + wave * 32 + l32;
+
+  // Q and tQ of this lane's query row, as B operands: k-step kk holds
+  // d = 16kk + 8hi .. 16kk + 8hi + 7.
+  bf16x8_t Qr[NKK], tQr[NKK];
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int64_t off = q_row * a.isl + kk * 16 + 8 * hi;
+      Qr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
+      tQr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
+    }
+  }
+
+  f32x16_t Oacc[NDB], ABacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
+  float m_run = -INFINITY;            // reference max (log2 units, scale folded in)
+  float l_part = 0.f, mu_part = 0.f;  // this lane's half of the row sums
+  const float sl2 = a.scale_log2, c = a.scale;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  for (int e = e0; e < e1; ++e) {
+    const Entry en = a.entries[e];
+    const uint64_t bits = en.pidx >= 0 ? a.bits[(int64_t)en.pidx * BM + wave * 32 + l32] : ~0ull;
+    for (int kt = en.kt0; kt < en.kt1; ++kt) {
+      __syncthreads();
+      stage_tile_bf16<D>(s, Kg, tKg, Vg, tVg, a.isl, kt * BN, L, tid);
+      __syncthreads();
+
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        // ---- scores and score tangents of 32 keys (transposed: lane = query) ----
+        f32x16_t S, TS;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = TS[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int off = (kb * 32 + l32) * Lds::KP + kk * 16 + 8 * hi;
+          const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(s.k + off));
+          const bf16x8_t tkop = as_bf16x8(*(const u32x4_t*)(s.tk + off));
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
+          TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
+          TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, tQr[kk], TS, 0, 0, 0);
+        }
+        // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
+
+        // ---- partial tile: masked-out pairs take no part (select; no tangent) ----
+        if (en.pidx >= 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = (bits >> key) & 1ull;
+            S[r] = ok ? S[r] : -INFINITY;
+            TS[r] = ok ? TS[r] : 0.f;
+          }
+        }
+
+        // ---- online softmax with lazy rescale ----
+        float mx = S[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const bool need = m_new > m_run + kLazyRescaleLog2;
+        if (__any(need)) {
+          const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+          m_run = need ? m_new : m_run;
+          l_part *= alpha;
+          mu_part *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              Oacc[db][r] *= alpha;
+              ABacc[db][r] *= alpha;
+            }
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+
+        // p~ = exp2(c log2e s - m); u = p~ * (c ts).  Both rounded to bf16 once;
+        // l and mu are summed from the rounded values.
+        bf16x8_t P[2], U[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int t = 0; t < 8; t += 2) {
+            const int r = 8 * st + t;
+            f32x2_t p, u;
+            p.x = fast_exp2(__builtin_fmaf(S[r], sl2, -m_use));
+            p.y = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -m_use));
+            u.x = p.x * (TS[r] * c);
+            u.y = p.y * (TS[r + 1] * c);
+            const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
+            const bf16x2_t ub = __builtin_convertvector(u, bf16x2_t);
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
+            mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+            P[st][t] = pb.x;
+            P[st][t + 1] = pb.y;
+            U[st][t] = ub.x;
+            U[st][t + 1] = ub.y;
+          }
+
+        // ---- value products (transposed: rows = d, cols = queries) ----
+        //   O~ += V^T P~^T ;  (A + B) += V^T U^T + tV^T P~^T
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int kbase = kb * 32 + 16 * st + 4 * hi;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int off = (db * 32 + l32) * Lds::VP + kbase;
+            u32x4_t vw, tvw;
+            const u32x2_t v0 = *(const u32x2_t*)(s.vt + off), v1 = *(const u32x2_t*)(s.vt + off + 8);
+            const u32x2_t t0 = *(const u32x2_t*)(s.tvt + off), t1 = *(const u32x2_t*)(s.tvt + off + 8);
+            vw.x = v0.x; vw.y = v0.y; vw.z = v1.x; vw.w = v1.y;
+            tvw.x = t0.x; tvw.y = t0.y; tvw.z = t1.x; tvw.w = t1.y;
+            const bf16x8_t vop = as_bf16x8(vw), tvop = as_bf16x8(tvw);
+            Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[st], Oacc[db], 0, 0, 0);
+            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, U[st], ABacc[db], 0, 0, 0);
+            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tvop, P[st], ABacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
+  const float l_tot = l_part + wave_xor32(l_part);
+  const float mu_tot = mu_part + wave_xor32(mu_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_row < L) {
+    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        f32x4_t ov, tv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          const float o = Oacc[db][r] * inv;
+          ov[j] = o;
+          tv[j] = (ABacc[db][r] - mu_tot * o) * inv;
+        }
+        if constexpr (OUT_F32) {
+          *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
+          *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+        } else {
+          *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
+          *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
+        }
+      }
+    if (hi == 0)
+      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: same decomposition with MFMA 32x32x2 fp32 and no rounding of
+// p~ or p~.ts.  V needs no transpose: with two keys per MFMA step each lane
+// reads one value of a key row.
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct F32Lds {
+  static constexpr int P = D + 4;
+  float k[BN * P];
+  float tk[BN * P];
+  float v[BN * P];
+  float tv[BN * P];
+};
+
+template <int D>
+__device__ __forceinline__ void stage_one_f32(float* __restrict__ dst, const float* __restrict__ src,
+                                              int64_t sl, int key0, int L, int tid) {
+  constexpr int CH = D / 4;  // 16-byte chunks per row
+  constexpr int N = BN * CH / NTHREADS;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t r[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int key = c / CH, col = (c % CH) * 4;
+    const int gk = key0 + key;
+    r[i] = gk < L ? *(const f32x4_t*)(src + gk * sl + col) : zero;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int key = c / CH, col = (c % CH) * 4;
+    *(f32x4_t*)(dst + key * F32Lds<D>::P + col) = r[i];
+  }
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
+void attn_jvp_fwd_f32_kernel(FwdArgs a) {
+  constexpr int NKK = D / 2;
+  constexpr int NDB = D / 32;
+  using Lds = F32Lds<D>;
+  __shared__ __attribute__((aligned(16))) Lds s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int qt = a.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const float* __restrict__ Qg = (const float*)a.q + in_off;
+  const float* __restrict__ Kg = (const float*)a.k + in_off;
+  const float* __restrict__ Vg = (const float*)a.v + in_off;
+  const float* __restrict__ tQg = (const float*)a.tq + in_off;
+  const float* __restrict__ tKg = (const float*)a.tk + in_off;
+  const float* __restrict__ tVg = (const float*)a.tv + in_off;
+  const int q_row = qt * BM + wave * 32 + l32;
+
+  float Qr[NKK], tQr[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int64_t off = q_row * a.isl + 2 * kk + hi;
+    Qr[kk] = q_row < L ? Qg[off] : 0.f;
+    tQr[kk] = q_row < L ? tQg[off] : 0.f;
+  }
+
+  f32x16_t Oacc[NDB], ABacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f, mu_part = 0.f;
+  const float sl2 = a.scale_log2, c = a.scale;
+
+  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  for (int e = e0; e < e1; ++e) {
+    const Entry en = a.entries[e];
+    const uint64_t bits = en.pidx >= 0 ? a.bits[(int64_t)en.pidx * BM + wave * 32 + l32] : ~0ull;
+    for (int kt = en.kt0; kt < en.kt1; ++kt) {
+      __syncthreads();
+      stage_one_f32<D>(s.k, Kg, a.isl, kt * BN, L, tid);
+      stage_one_f32<D>(s.tk, tKg, a.isl, kt * BN, L, tid);
+      stage_one_f32<D>(s.v, Vg, a.isl, kt * BN, L, tid);
+      stage_one_f32<D>(s.tv, tVg, a.isl, kt * BN, L, tid);
+      __syncthreads();
+
+#pragma unroll 1
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        f32x16_t S, TS;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = TS[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int off = (kb * 32 + l32) * Lds::P + 2 * kk + hi;
+          const float kop = s.k[off], tkop = s.tk[off];
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, Qr[kk], S, 0, 0, 0);
+          TS = __builtin_amdgcn_mfma_f32_32x32x2f32(tkop, Qr[kk], TS, 0, 0, 0);
+          TS = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, tQr[kk], TS, 0, 0, 0);
+        }
+        if (en.pidx >= 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = (bits >> key) & 1ull;
+            S[r] = ok ? S[r] : -INFINITY;
+            TS[r] = ok ? TS[r] : 0.f;
+          }
+        }
+        float mx = S[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const bool need = m_new > m_run + kLazyRescaleLog2;
+        if (__any(need)) {
+          const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+          m_run = need ? m_new : m_run;
+          l_part *= alpha;
+          mu_part *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              Oacc[db][r] *= alpha;
+              ABacc[db][r] *= alpha;
+            }
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float P[16], U[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          P[r] = fast_exp2(__builtin_fmaf(S[r], sl2, -m_use));
+          U[r] = P[r] * (TS[r] * c);
+          l_part += P[r];
+          mu_part += U[r];
+        }
+        // two keys per MFMA step: lanes hi = 0 / 1 supply key 8*(r/4) + 4*hi + r%4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int off = key * Lds::P + db * 32 + l32;
+            const float vop = s.v[off], tvop = s.tv[off];
+            Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, P[r], Oacc[db], 0, 0, 0);
+            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, U[r], ABacc[db], 0, 0, 0);
+            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(tvop, P[r], ABacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  const float l_tot = l_part + wave_xor32(l_part);
+  const float mu_tot = mu_part + wave_xor32(mu_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_row < L) {
+    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        f32x4_t ov, tv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          const float o = Oacc[db][r] * inv;
+          ov[j] = o;
+          tv[j] = (ABacc[db][r] - mu_tot * o) * inv;
+        }
+        *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
+        *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+      }
+    if (hi == 0)
+      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, hipStream_t stream) {
+  const int64_t grid64 = int64_t(a.n_tasks) * a.B * a.H;
+  if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
+  const dim3 grid((unsigned)grid64), block(NTHREADS);
+  if (in_dtype == AJ_BF16) {
+    if (out_dtype == AJ_BF16) {
+      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    } else {
+      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    }
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<128>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<64>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? AJ_OK : AJ_EHIP;
+}
+
+}  // namespace aj

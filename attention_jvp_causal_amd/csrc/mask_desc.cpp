@@ -1,0 +1,202 @@
+// Host-side mask descriptor: frame-level layouts -> admissible rectangles ->
+// tile-level skip / partial / full map -> longest-first task list.
+//
+// "Causal-rCM", App. B ("Sparse custom-mask representation"): the custom mask
+// is a set of query groups, each a contiguous query interval with a list of
+// admissible key intervals; each task streams only the key ranges of its group.
+// Here a query group is a kernel query tile, and its key ranges are stored as
+// runs of full key tiles plus single partial tiles carrying per-row bitmasks,
+// so the kernel never evaluates a mask predicate on a full tile.
+#include <algorithm>
+#include <map>
+#include <new>
+#include <vector>
+
+#include "aj_internal.h"
+
+namespace aj {
+
+namespace {
+
+int32_t validate_rects(int32_t L, const int32_t* r, int32_t n) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t q0 = r[4 * i], q1 = r[4 * i + 1], k0 = r[4 * i + 2], k1 = r[4 * i + 3];
+    if (q0 < 0 || q0 >= q1 || q1 > L || k0 < 0 || k0 >= k1 || k1 > L) return AJ_EMASK;
+  }
+  // pairwise disjointness: sort by q0, compare only rectangles whose query
+  // ranges overlap
+  std::vector<int32_t> order(n);
+  for (int32_t i = 0; i < n; ++i) order[i] = i;
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return r[4 * a] < r[4 * b]; });
+  for (int32_t x = 0; x < n; ++x) {
+    const int32_t* a = r + 4 * order[x];
+    for (int32_t y = x + 1; y < n; ++y) {
+      const int32_t* b = r + 4 * order[y];
+      if (b[0] >= a[1]) break;
+      if (b[2] < a[3] && a[2] < b[3]) return AJ_EMASK;
+    }
+  }
+  return AJ_OK;
+}
+
+struct RectRef {
+  int32_t q0, q1, k0, k1;
+};
+
+}  // namespace
+
+int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out) {
+  if (s->num_frames < 1 || s->frame_tokens < 1 || s->frames_per_chunk < 1) return AJ_EMASK;
+  const int64_t half = int64_t(s->num_frames) * s->frame_tokens;
+  const int64_t want = s->kind == AJ_MASK_TF_CLEAN_NOISY ? 2 * half : half;
+  if (s->kind != AJ_MASK_FULL && s->kind != AJ_MASK_BLOCK_CAUSAL && s->kind != AJ_MASK_TF_CLEAN_NOISY)
+    return AJ_EMASK;
+  if (want != L) return AJ_EMASK;
+  const int64_t C = int64_t(s->frames_per_chunk) * s->frame_tokens;  // tokens per chunk
+  const int64_t nchunks = (half + C - 1) / C;
+  auto push = [&](int64_t q0, int64_t q1, int64_t k0, int64_t k1) {
+    if (q0 < q1 && k0 < k1) {
+      out->push_back(int32_t(q0));
+      out->push_back(int32_t(q1));
+      out->push_back(int32_t(k0));
+      out->push_back(int32_t(k1));
+    }
+  };
+  out->clear();
+  if (s->kind == AJ_MASK_FULL) {
+    push(0, L, 0, L);
+    return AJ_OK;
+  }
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t b = c * C, e = std::min(half, (c + 1) * C);
+    // own chunk and all earlier chunks (clean stream for teacher forcing)
+    push(b, e, 0, e);
+    if (s->kind == AJ_MASK_TF_CLEAN_NOISY) {
+      push(half + b, half + e, 0, b);            // strictly earlier clean chunks
+      push(half + b, half + e, half + b, half + e);  // own noisy chunk
+    }
+  }
+  return AJ_OK;
+}
+
+int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,
+                         aj_mask_desc** out) {
+  if (!out) return AJ_EINVAL;
+  *out = nullptr;
+  if (L < 1 || n < 0 || (n > 0 && !r)) return AJ_EINVAL;
+  if (!supported_head_dim(head_dim) || !supported_dtype(dtype)) return AJ_ENOTSUP;
+  int32_t st = validate_rects(L, r, n);
+  if (st != AJ_OK) return st;
+
+  aj_mask_desc* d = new (std::nothrow) aj_mask_desc();
+  if (!d) return AJ_ENOMEM;
+  try {
+    const int32_t BM = kTileM, BN = kTileN;
+    d->seq_len = L;
+    d->head_dim = head_dim;
+    d->dtype = dtype;
+    d->n_qt = (L + BM - 1) / BM;
+    d->n_kt = (L + BN - 1) / BN;
+
+    // bucket rectangles by the query tiles they touch
+    std::vector<std::vector<RectRef>> per_qt(d->n_qt);
+    for (int32_t i = 0; i < n; ++i) {
+      RectRef x{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+      d->pairs += int64_t(x.q1 - x.q0) * (x.k1 - x.k0);
+      for (int32_t qt = x.q0 / BM; qt <= (x.q1 - 1) / BM; ++qt) per_qt[qt].push_back(x);
+    }
+
+    std::vector<int64_t> work(d->n_qt, 0);
+    d->qt_off.assign(d->n_qt + 1, 0);
+    for (int32_t qt = 0; qt < d->n_qt; ++qt) {
+      d->qt_off[qt] = int32_t(d->entries.size());
+      const int32_t a = qt * BM, b = std::min(L, a + BM);
+      const int64_t full_count = int64_t(b - a) * BN;  // allowed pairs in a full tile
+      // allowed-pair count per key tile: runs of interior tiles go into a
+      // difference map, the (at most two) boundary tiles of each rectangle
+      // into a point map
+      std::map<int32_t, int64_t> run_delta, points;
+      for (const RectRef& x : per_qt[qt]) {
+        const int64_t rows = std::min(b, x.q1) - std::max(a, x.q0);
+        const int32_t kf = x.k0 / BN, kl = (x.k1 - 1) / BN;
+        if (kf == kl) {
+          points[kf] += rows * (x.k1 - x.k0);
+          continue;
+        }
+        points[kf] += rows * (int64_t(kf + 1) * BN - x.k0);
+        points[kl] += rows * (x.k1 - int64_t(kl) * BN);
+        if (kl > kf + 1) {
+          run_delta[kf + 1] += rows * BN;
+          run_delta[kl] -= rows * BN;
+        }
+      }
+      // sweep over breakpoints in key-tile order
+      std::vector<int32_t> cuts;
+      for (auto& kv : run_delta) cuts.push_back(kv.first);
+      for (auto& kv : points) {
+        cuts.push_back(kv.first);
+        cuts.push_back(kv.first + 1);
+      }
+      std::sort(cuts.begin(), cuts.end());
+      cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+      int64_t run = 0;
+      auto rd = run_delta.begin();
+      for (size_t ci = 0; ci + 1 < cuts.size(); ++ci) {
+        const int32_t s0 = cuts[ci], s1 = cuts[ci + 1];
+        while (rd != run_delta.end() && rd->first <= s0) run += (rd++)->second;
+        auto pt = points.find(s0);
+        const bool is_point = pt != points.end();
+        const int64_t cnt = run + (is_point ? pt->second : 0);
+        // cuts include p and p + 1 for every point tile p, so a point segment
+        // is exactly one tile wide
+        const int32_t e1 = s1;
+        if (cnt == 0) continue;
+        const bool in_range = int64_t(e1) * BN <= L;
+        if (cnt == full_count && in_range) {
+          if (!d->entries.empty() && int32_t(d->entries.size()) > d->qt_off[qt] &&
+              d->entries.back().pidx < 0 && d->entries.back().kt1 == s0)
+            d->entries.back().kt1 = e1;  // extend the previous full run
+          else
+            d->entries.push_back(Entry{s0, e1, -1, 0});
+          d->full_tiles += e1 - s0;
+        } else {
+          for (int32_t kt = s0; kt < e1; ++kt) {
+            const int32_t pidx = d->partial_tiles++;
+            d->entries.push_back(Entry{kt, kt + 1, pidx, 0});
+            d->bits.resize(size_t(d->partial_tiles) * BM, 0);
+            uint64_t* rowbits = &d->bits[size_t(pidx) * BM];
+            const int32_t key0 = kt * BN;
+            for (const RectRef& x : per_qt[qt]) {
+              const int32_t kk0 = std::max(x.k0, key0), kk1 = std::min(x.k1, key0 + BN);
+              if (kk0 >= kk1) continue;
+              const int32_t w = kk1 - kk0;
+              const uint64_t m = (w == 64 ? ~0ull : ((1ull << w) - 1)) << (kk0 - key0);
+              for (int32_t q = std::max(a, x.q0); q < std::min(b, x.q1); ++q) rowbits[q - a] |= m;
+            }
+          }
+        }
+      }
+      for (int32_t e = d->qt_off[qt]; e < int32_t(d->entries.size()); ++e)
+        work[qt] += d->entries[e].kt1 - d->entries[e].kt0;
+    }
+    d->qt_off[d->n_qt] = int32_t(d->entries.size());
+
+    // tasks: every query tile (tiles with no allowed key still write zeros),
+    // most visited key tiles first; ties by larger tile index
+    d->tasks.resize(d->n_qt);
+    for (int32_t qt = 0; qt < d->n_qt; ++qt) d->tasks[qt] = qt;
+    std::stable_sort(d->tasks.begin(), d->tasks.end(), [&](int32_t x, int32_t y) {
+      return work[x] != work[y] ? work[x] > work[y] : x > y;
+    });
+  } catch (const std::bad_alloc&) {
+    delete d;
+    return AJ_ENOMEM;
+  } catch (...) {
+    delete d;
+    return AJ_EINVAL;
+  }
+  *out = d;
+  return AJ_OK;
+}
+
+}  // namespace aj

@@ -1,0 +1,176 @@
+/*
+ * attn_jvp.h - C ABI of the MI355X (gfx950) custom-mask attention-JVP library.
+ *
+ * The operation ("Causal-rCM: A Unified Teacher-Forcing and Self-Forcing Open
+ * Recipe for Autoregressive Diffusion Distillation", App. B, "FlashAttention-2
+ * JVP Kernel with Custom Masks"): for every (batch, head), given primal Q, K, V,
+ * tangents tQ, tK, tV and a mask M of admissible (query, key) pairs,
+ *
+ *   s_ij  = scale * <q_i, k_j>                       masked softmax attention (Eq. 42)
+ *   ts_ij = scale * (<tq_i, k_j> + <q_i, tk_j>)       score tangent (Eq. 43)
+ *   P_ij  = softmax_j over allowed keys of s_ij;  O_i = sum_j P_ij v_j
+ *   tO_i  = sum_j P_ij (ts_ij - sum_k P_ik ts_ik) v_j + sum_j P_ij tv_j   (Eq. 44)
+ *   lse_i = log sum_j exp(s_ij)  over allowed keys (natural log)
+ *
+ * The mask has no tangent: masked-out pairs take part in neither O nor tO.
+ * The kernel evaluates Eq. 44 in the online-softmax form of Eq. 45 in a single
+ * streaming pass over the admissible rectangles of the mask (App. B,
+ * "Sparse custom-mask representation").
+ *
+ * Tensor layout: [B, H, L, D] with D contiguous (the per-rank layout of the
+ * attention in Sec. 3.2.1); lse is [B, H, L] float32, contiguous.
+ *
+ * Conventions for every entry point:
+ *  - Return value is an aj_status; AJ_OK (0) on success.
+ *  - All argument checks happen before any device work is enqueued; on error
+ *    nothing is written and nothing is launched.
+ *  - No C++ exception crosses this boundary.
+ *  - Device pointers are owned by the caller; the library never frees or
+ *    retains them.  Mask descriptors are owned by the library (create with a
+ *    builder, release with attn_jvp_mask_desc_free).
+ */
+#ifndef ATTN_JVP_H_
+#define ATTN_JVP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AJ_OK = 0,
+  AJ_EINVAL = 1,   /* bad argument: null/misaligned pointer, bad size or stride, non-finite scale */
+  AJ_ENOTSUP = 2,  /* valid but unsupported: head_dim not in {64, 128}, dtype pair not built */
+  AJ_ENOMEM = 3,   /* host or device allocation failed */
+  AJ_EHIP = 4,     /* a HIP runtime call failed (no device, launch failure, ...) */
+  AJ_EMASK = 5     /* mask specification invalid, or descriptor does not match the call */
+} aj_status;
+
+/* Element types of Q, K, V, tQ, tK, tV (in) and O, tO (out). */
+typedef enum { AJ_F32 = 0, AJ_BF16 = 1 } aj_dtype;
+
+/* Frame-level mask layouts (Sec. 2.3, Sec. 3.1.1 / Eq. 8 and the c1-1 / c3-3
+ * chunk patterns of Sec. 5).  Tokens are laid out frame after frame, each frame
+ * frame_tokens contiguous tokens; a chunk is frames_per_chunk frames (the last
+ * chunk may be shorter).  Attention inside a chunk is always full.
+ *  AJ_MASK_FULL            every query sees every key (L = num_frames * frame_tokens)
+ *  AJ_MASK_BLOCK_CAUSAL    a query sees keys of its own chunk and all earlier
+ *                          chunks; frames_per_chunk = 1 is frame-causal
+ *  AJ_MASK_TF_CLEAN_NOISY  packed [clean | noisy] teacher-forcing sequence,
+ *                          L = 2 * num_frames * frame_tokens: clean chunk i sees
+ *                          clean chunks <= i; noisy chunk i sees clean chunks
+ *                          < i and its own noisy chunk */
+typedef enum {
+  AJ_MASK_FULL = 0,
+  AJ_MASK_BLOCK_CAUSAL = 1,
+  AJ_MASK_TF_CLEAN_NOISY = 2
+} aj_mask_kind;
+
+typedef struct {
+  int32_t kind;              /* aj_mask_kind */
+  int32_t num_frames;        /* frames (per half for AJ_MASK_TF_CLEAN_NOISY), >= 1 */
+  int32_t frame_tokens;      /* tokens per frame, >= 1 */
+  int32_t frames_per_chunk;  /* >= 1 */
+} aj_mask_spec;
+
+/* Opaque descriptor: the mask as a tile-level skip / partial / full map over
+ * the kernel's query and key tiles, per-row key bitmasks for partial tiles and
+ * a longest-first task order.  Immutable after creation; may be shared by
+ * threads and streams.  Device copies of its tables are made on first use on
+ * each device and freed by attn_jvp_mask_desc_free. */
+typedef struct aj_mask_desc aj_mask_desc;
+
+typedef struct {
+  int64_t unmasked_pairs;   /* allowed (query, key) pairs per (batch, head) */
+  int32_t seq_len;
+  int32_t tile_m;           /* query rows per tile */
+  int32_t tile_n;           /* keys per tile */
+  int32_t num_q_tiles;
+  int32_t num_k_tiles;
+  int32_t full_tiles;       /* tiles with every (query < L, key) pair allowed */
+  int32_t partial_tiles;    /* tiles with some, not all, pairs allowed */
+  int32_t num_entries;      /* span entries over all query tiles */
+} aj_mask_stats;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_jvp_status_str(int32_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t attn_jvp_version(void);
+
+/* Build a descriptor for a frame-level layout.
+ * seq_len must equal the layout's length (see aj_mask_kind); head_dim and dtype
+ * select the kernel whose tile geometry the map is built for.
+ * Host-only: touches no device.  Errors: AJ_EINVAL (null out, bad sizes),
+ * AJ_EMASK (unknown kind, seq_len mismatch), AJ_ENOTSUP (head_dim/dtype),
+ * AJ_ENOMEM.  On error *out is set to NULL. */
+int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int32_t head_dim,
+                                 int32_t dtype, aj_mask_desc** out);
+
+/* Build a descriptor from admissible rectangles (App. B: a mask as a list of
+ * query-key rectangles).  rects holds n_rects * 4 int32 values
+ * {q0, q1, k0, k1} per rectangle, each half-open, inside [0, seq_len), with
+ * q0 < q1 and k0 < k1; rectangles must be pairwise disjoint.  n_rects may be 0
+ * (nothing allowed).  Host-only.  Errors as for attn_jvp_mask_desc_build; an
+ * overlap or out-of-range rectangle gives AJ_EMASK. */
+int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
+                                      int32_t head_dim, int32_t dtype, aj_mask_desc** out);
+
+/* Summary of a descriptor.  Errors: AJ_EINVAL on null arguments. */
+int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* desc, aj_mask_stats* out);
+
+/* Classification of tile (q_tile, k_tile): *kind = 0 skip, 1 partial, 2 full.
+ * Errors: AJ_EINVAL on null arguments or out-of-range tile indices. */
+int32_t attn_jvp_mask_desc_tile_kind(const aj_mask_desc* desc, int32_t q_tile, int32_t k_tile,
+                                     int32_t* kind);
+
+/* Key bitmask of one query row of a tile: bit j set when key
+ * k_tile * tile_n + j is allowed for query q_tile * tile_m + row.  For full
+ * tiles all tile_n bits are set, for skipped tiles none.
+ * Errors: AJ_EINVAL on null arguments or out-of-range indices. */
+int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* desc, int32_t q_tile, int32_t k_tile,
+                                    int32_t row, uint64_t* bits);
+
+/* Release a descriptor and its device tables on every device that used it.
+ * Must not be called while a launch that uses it may still run.  NULL is a
+ * no-op. */
+void attn_jvp_mask_desc_free(aj_mask_desc* desc);
+
+/* Shapes and strides of one call.  Strides are in elements.  The six inputs
+ * share in_stride_{b,h,l}; O and tO share out_stride_{b,h,l}; the D axis is
+ * contiguous for all of them.  lse is a contiguous [B, H, L] float32 array. */
+typedef struct {
+  int32_t batch;      /* B >= 1 */
+  int32_t heads;      /* H >= 1 */
+  int32_t seq_len;    /* L >= 1, equal to the descriptor's */
+  int32_t head_dim;   /* D in {64, 128} */
+  int32_t in_dtype;   /* aj_dtype */
+  int32_t out_dtype;  /* aj_dtype: AJ_BF16 needs in_dtype AJ_BF16; AJ_F32 is accepted for both */
+  int64_t in_stride_b, in_stride_h, in_stride_l;
+  int64_t out_stride_b, out_stride_h, out_stride_l;
+} aj_shape;
+
+/* Forward-mode JVP of masked attention: writes O, tO ([B, H, L, D], out_dtype)
+ * and lse ([B, H, L] float32) for inputs q, k, v, tq, tk, tv ([B, H, L, D],
+ * in_dtype), all device pointers, 16-byte aligned, strides multiples of
+ * 16 bytes / element size.  scale multiplies the scores and their tangents;
+ * pass 1/sqrt(D) for the usual softmax scale.  Rows with no allowed key get
+ * O = tO = 0 and lse = -inf.  Input values at masked-out positions must be
+ * finite (they are read for partial tiles and multiplied by zero).
+ * The outputs must not overlap the inputs.
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and runs
+ * asynchronously; device faults surface at the caller's next synchronisation.
+ * The first call on a device with a given descriptor uploads its tables
+ * (synchronous hipMalloc/hipMemcpy, once).
+ * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK (desc seq_len / head_dim / dtype
+ * differ from the call), AJ_EHIP, AJ_ENOMEM. */
+int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const void* v,
+                     const void* tq, const void* tk, const void* tv, const aj_mask_desc* mask,
+                     float scale, void* o, void* to, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H_ */

@@ -31,18 +31,13 @@ from .masks import key_ranges
 _ROW_BLOCK = 256  # rows per dense block, bounds memory at ~L * 256 * 8 bytes per matrix
 
 
-def _row_groups(mask, rows: Sequence[int]) -> List[Tuple[List[int], List[Tuple[int, int]]]]:
-    """Split the requested rows into runs that share one allowed-key set."""
-    groups: List[Tuple[List[int], List[Tuple[int, int]]]] = []
-    prev = None
+def _row_groups(mask, rows: Sequence[int]):
+    """Group the requested rows by their allowed-key set (order of first use)."""
+    groups = {}
     for i in rows:
-        kr = key_ranges(mask, int(i))
-        if groups and kr == prev and int(i) == groups[-1][0][-1] + 1 and len(groups[-1][0]) < _ROW_BLOCK:
-            groups[-1][0].append(int(i))
-        else:
-            groups.append(([int(i)], kr))
-        prev = kr
-    return groups
+        kr = tuple(key_ranges(mask, int(i)))
+        groups.setdefault(kr, []).append(int(i))
+    return [(g, list(kr)) for kr, g in groups.items()]
 
 
 def _gather_keys(x: np.ndarray, ranges: List[Tuple[int, int]]) -> np.ndarray:
@@ -79,22 +74,24 @@ def attn_jvp_ref(q, k, v, tq, tk, tv, mask, scale: Optional[float] = None,
         nk = sum(b - a for a, b in ranges)
         if nk == 0:
             continue  # no allowed key: O = tO = 0, lse = -inf
-        out_idx = [pos[r][0] for r in grp]
         for b_ in range(B):
             for h in range(H):
-                Q, TQ = q[b_, h, grp], tq[b_, h, grp]
                 K, TK = _gather_keys(k[b_, h], ranges), _gather_keys(tk[b_, h], ranges)
                 V, TV = _gather_keys(v[b_, h], ranges), _gather_keys(tv[b_, h], ranges)
-                s = c * (Q @ K.T)
-                ts = c * (TQ @ K.T + Q @ TK.T)
-                m = s.max(axis=1, keepdims=True)
-                e = np.exp(s - m)
-                l = e.sum(axis=1, keepdims=True)
-                P = e / l
-                mu = (P * ts).sum(axis=1, keepdims=True)
-                o[b_, h, out_idx] = P @ V
-                to[b_, h, out_idx] = (P * (ts - mu)) @ V + P @ TV
-                lse[b_, h, out_idx] = m[:, 0] + np.log(l[:, 0])
+                for r0 in range(0, len(grp), _ROW_BLOCK):
+                    blk = grp[r0:r0 + _ROW_BLOCK]
+                    out_idx = [pos[r][0] for r in blk]
+                    Q, TQ = q[b_, h, blk], tq[b_, h, blk]
+                    s = c * (Q @ K.T)
+                    ts = c * (TQ @ K.T + Q @ TK.T)
+                    m = s.max(axis=1, keepdims=True)
+                    e = np.exp(s - m)
+                    l = e.sum(axis=1, keepdims=True)
+                    P = e / l
+                    mu = (P * ts).sum(axis=1, keepdims=True)
+                    o[b_, h, out_idx] = P @ V
+                    to[b_, h, out_idx] = (P * (ts - mu)) @ V + P @ TV
+                    lse[b_, h, out_idx] = m[:, 0] + np.log(l[:, 0])
     # duplicated requested rows (rare) copy the first computed result
     for r, ns in pos.items():
         for n in ns[1:]:

@@ -1,0 +1,75 @@
+"""Helpers for the GPU parity tests: run the HIP path and the oracle on the
+same seeded inputs and compare with the stated tolerances."""
+import numpy as np
+
+from attention_jvp_causal_amd.workloads import Workload, make_inputs, as_float64
+from oracle import MaskLayout, attn_jvp_ref
+
+# Tolerances for the HIP path against the fp64 oracle:
+#  fp32 inputs: rel-L2 <= 1e-5; bf16 inputs: rel-L2 <= 1e-2 and max-abs <= 5e-2.
+TOL = {"f32": {"rel_l2": 1e-5, "max_abs": None}, "bf16": {"rel_l2": 1e-2, "max_abs": 5e-2}}
+
+
+def rel_l2(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.linalg.norm(y)
+    return float(np.linalg.norm(x - y) / (den if den > 0 else 1.0))
+
+
+def max_abs(x, y):
+    return float(np.max(np.abs(np.asarray(x, np.float64) - np.asarray(y, np.float64)))) if np.size(y) else 0.0
+
+
+def oracle_mask(w: Workload) -> MaskLayout:
+    return MaskLayout(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk)
+
+
+def run_gpu(w: Workload, inputs=None, out_dtype=None, device="cuda"):
+    import torch
+    import attention_jvp_causal_amd as aj
+
+    if inputs is None:
+        inputs = make_inputs(w)
+    dev = {n: t.to(device) for n, t in inputs.items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    o, to, lse = aj.attn_jvp_fwd(dev["q"], dev["k"], dev["v"], dev["tq"], dev["tk"], dev["tv"], desc,
+                                 scale=w.scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return inputs, desc, (o, to, lse)
+
+
+def to_np(t):
+    import torch
+
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare(w: Workload, got, ref, label=""):
+    """Returns a dict of errors and asserts the tolerances for O, tO and lse."""
+    tol = TOL[w.dtype]
+    res = {}
+    for name, g, r in zip(("o", "to", "lse"), got, ref):
+        finite = np.isfinite(r)
+        assert np.array_equal(np.isfinite(g), finite), f"{label} {name}: non-finite pattern differs"
+        gg, rr = g[finite], r[finite]
+        res[name] = (rel_l2(gg, rr), max_abs(gg, rr))
+        assert res[name][0] <= tol["rel_l2"], f"{label} {name}: rel-L2 {res[name][0]:.3e} > {tol['rel_l2']}"
+        if tol["max_abs"] is not None:
+            assert res[name][1] <= tol["max_abs"], f"{label} {name}: max-abs {res[name][1]:.3e} > {tol['max_abs']}"
+    return res
+
+
+def sample_rows(w: Workload, n_random=40, seed=0):
+    """Rows at every frame edge, query-tile edges near frames, the ragged end,
+    plus random rows."""
+    L, F = w.seq_len, w.frame_tokens
+    rows = {0, L - 1}
+    for f in range(L // F):
+        rows |= {f * F, f * F + F - 1}
+    for qt in (1, (L // 128) // 2, L // 128 - 1):
+        rows |= {qt * 128 - 1, qt * 128}
+    rng = np.random.default_rng(seed)
+    rows |= set(int(x) for x in rng.integers(0, L, size=n_random))
+    return sorted(r for r in rows if 0 <= r < L)

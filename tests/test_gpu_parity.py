@@ -1,0 +1,165 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Reduced sizes (oracle over every element) span several query and key tiles
+with ragged tails; the full measured workloads are checked on sampled rows
+in the same launch configuration bench.py times (bf16 outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from attention_jvp_causal_amd.workloads import WORKLOADS, Workload, as_float64, make_inputs, with_shape
+from oracle import attn_jvp_ref
+from parity_util import compare, oracle_mask, run_gpu, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_compare(w, out_dtype=None):
+    print(f"[case] {w.name} B={w.batch} H={w.heads} L={w.seq_len} D={w.head_dim} {w.dtype} "
+          f"{w.mask_kind} T={w.num_frames} F={w.frame_tokens} c={w.frames_per_chunk} out={out_dtype}", flush=True)
+    inputs, desc, got = run_gpu(w, out_dtype=out_dtype)
+    x = as_float64(inputs)
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale)
+    res = compare(w, [to_np(t) for t in got], ref, label=w.name)
+    print(f"[ok] {w.name}: " + ", ".join(f"{k} relL2={v[0]:.2e} maxabs={v[1]:.2e}" for k, v in res.items()), flush=True)
+    return inputs, got, ref
+
+
+def test_tiny_frame_causal_f32_exact_workload():
+    _full_compare(WORKLOADS["tiny_frame_causal_f32"])
+
+
+REDUCED = [
+    # name, kind, T, F, c, B, H, D, dtype, sigmas
+    ("fc_bf16_d128", "block_causal", 5, 100, 1, 1, 2, 128, "bf16", (1, 1, 1)),
+    ("c2_bf16_d128_ragged", "block_causal", 7, 61, 2, 2, 1, 128, "bf16", (1, 1, 1)),
+    ("c3_bf16_d64", "block_causal", 6, 88, 3, 1, 3, 64, "bf16", (1, 1, 1)),
+    ("stress_bf16_d64", "block_causal", 6, 88, 3, 2, 2, 64, "bf16", (3, 1, 0.5)),
+    ("tf_bf16_d128", "tf_clean_noisy", 4, 90, 1, 1, 2, 128, "bf16", (1, 1, 1)),
+    ("tf_c2_bf16_d64", "tf_clean_noisy", 5, 47, 2, 1, 2, 64, "bf16", (1, 1, 1)),
+    ("full_bf16_d128", "full", 3, 150, 1, 1, 2, 128, "bf16", (1, 1, 1)),
+    ("fc_f32_d128", "block_causal", 5, 100, 1, 1, 2, 128, "f32", (1, 1, 1)),
+    ("tf_f32_d64", "tf_clean_noisy", 4, 45, 1, 2, 1, 64, "f32", (1, 1, 1)),
+    ("c3_f32_d64_stress", "block_causal", 6, 40, 3, 1, 2, 64, "f32", (3, 1, 0.5)),
+    ("small_L_bf16", "block_causal", 3, 7, 1, 1, 1, 128, "bf16", (1, 1, 1)),
+    ("small_L_f32", "full", 1, 33, 1, 1, 1, 64, "f32", (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
+def test_reduced_sizes_every_element(case):
+    name, kind, T, F, c, B, H, D, dt, (sq, sv, st) = case
+    w = Workload(name, B, H, D, dt, kind, T, F, c, seed=100 + REDUCED.index(case), sigma_qk=sq, sigma_v=sv,
+                 sigma_t=st, clean_tangent_zero=(kind == "tf_clean_noisy"))
+    _full_compare(w)
+
+
+@pytest.mark.parametrize("case", ["fc_bf16_d128", "stress_bf16_d64"])
+def test_bf16_inputs_fp32_outputs(case):
+    name, kind, T, F, c, B, H, D, dt, (sq, sv, st) = [x for x in REDUCED if x[0] == case][0]
+    w = Workload(name, B, H, D, dt, kind, T, F, c, seed=7, sigma_qk=sq, sigma_v=sv, sigma_t=st)
+    inputs, got, ref = _full_compare(w, out_dtype=torch.float32)
+    assert got[0].dtype == torch.float32
+
+
+@pytest.mark.parametrize("wname", ["wan13b_frame_causal", "wan13b_chunk3_causal", "wan13b_tf_clean_noisy",
+                                   "stress_chunk3_d64"])
+def test_full_size_workloads_sampled_rows(wname):
+    w = WORKLOADS[wname]
+    print(f"[case] full-size {wname} shape={w.shape} {w.dtype}", flush=True)
+    inputs, desc, got = run_gpu(w)
+    o, to, lse = got
+    # whole-tensor properties
+    assert torch.isfinite(o).all() and torch.isfinite(to).all() and torch.isfinite(lse).all()
+    if w.clean_tangent_zero:
+        half = w.seq_len // 2
+        assert (to[:, :, :half] == 0).all(), "clean rows must have exactly zero tangent"
+    rows = sample_rows(w)
+    x = {n: t.to(torch.float64).numpy() for n, t in inputs.items()}
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale, rows=rows)
+    g = [to_np(o[:, :, rows]), to_np(to[:, :, rows]), to_np(lse[:, :, rows])]
+    res = compare(w, g, ref, label=wname)
+    print(f"[ok] {wname} rows={len(rows)}: " + ", ".join(f"{k} relL2={v[0]:.2e} maxabs={v[1]:.2e}"
+                                                         for k, v in res.items()), flush=True)
+
+
+def _w(kind="block_causal", T=5, F=100, c=1, B=1, H=2, D=128, dt="bf16", seed=11):
+    return Workload("inv", B, H, D, dt, kind, T, F, c, seed=seed)
+
+
+def test_invariants_on_gpu():
+    import attention_jvp_causal_amd as aj
+
+    w = _w()
+    inputs = {n: t.cuda() for n, t in make_inputs(w).items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    q, k, v, tq, tk, tv = (inputs[n] for n in ("q", "k", "v", "tq", "tk", "tv"))
+    f = lambda *a: aj.attn_jvp_fwd(*a, desc)
+    o1, to1, lse1 = f(q, k, v, tq, tk, tv)
+    # determinism: bitwise identical reruns
+    o2, to2, lse2 = f(q, k, v, tq, tk, tv)
+    assert torch.equal(o1, o2) and torch.equal(to1, to2) and torch.equal(lse1, lse2)
+    # tangent scaling by 2 is exact in binary floating point
+    _, to_2, _ = f(q, k, v, 2 * tq, 2 * tk, 2 * tv)
+    assert torch.equal(to_2, 2 * to1)
+    # zero tangents: tO == 0 exactly, primal unchanged
+    z = torch.zeros_like(q)
+    o0, to0, _ = f(q, k, v, z, z, z)
+    assert torch.equal(o0, o1) and (to0 == 0).all()
+    # tq = tk = 0: tO equals the primal output with v := tv
+    _, to_v, _ = f(q, k, v, z, z, tv)
+    o_tv, _, _ = f(q, k, tv, z, z, z)
+    assert torch.equal(to_v, o_tv)
+    # perturbing keys a row may not see changes nothing in that row:
+    # block-causal, rows of frame 0 never see keys of frames >= 1
+    F = w.frame_tokens
+    k2, v2, tk2, tv2 = (x.clone() for x in (k, v, tk, tv))
+    for x in (k2, v2, tk2, tv2):
+        x[:, :, F:] += 3.0
+    o3, to3, lse3 = f(q, k2, v2, tq, tk2, tv2)
+    assert torch.equal(o3[:, :, :F], o1[:, :, :F]) and torch.equal(to3[:, :, :F], to1[:, :, :F])
+    assert torch.equal(lse3[:, :, :F], lse1[:, :, :F])
+    assert not torch.equal(o3[:, :, F:], o1[:, :, F:])
+
+
+def test_rows_without_allowed_keys_and_rect_masks():
+    import attention_jvp_causal_amd as aj
+
+    L, D = 300, 64
+    rects = [(0, 100, 0, 100), (130, 300, 0, 40), (130, 300, 150, 300)]  # rows 100..129 see nothing
+    w = Workload("rects", 1, 2, D, "bf16", "full", 1, L, 1, seed=21)
+    inputs = make_inputs(w)
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    desc = aj.attn_jvp_mask_desc_from_rects(L, rects, head_dim=D, dtype="bf16")
+    o, to, lse = aj.attn_jvp_fwd(*(dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")), desc)
+    torch.cuda.synchronize()
+    from oracle import RectMask
+
+    x = as_float64(inputs)
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], RectMask(L, tuple(rects)))
+    assert (o[:, :, 100:130] == 0).all() and (to[:, :, 100:130] == 0).all()
+    assert torch.isneginf(lse[:, :, 100:130]).all()
+    compare(w, [to_np(o), to_np(to), to_np(lse)], ref, label="rects")
+
+
+def test_strided_inputs_and_outputs():
+    import attention_jvp_causal_amd as aj
+
+    w = _w(T=3, F=70, c=1, B=2, H=3, D=64, seed=31)
+    inputs = make_inputs(w)
+    # [B, L, H, D] storage viewed as [B, H, L, D]
+    dev = {n: t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3) for n, t in inputs.items()}
+    assert dev["q"].stride(2) == w.heads * w.head_dim
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    B, H, L, D = w.shape
+    ob = torch.empty((B, L, H, D), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
+    tob = torch.empty_like(ob)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    o, to, lse = aj.attn_jvp_fwd(*(dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")), desc, out=(ob, tob, lse))
+    torch.cuda.synchronize()
+    x = as_float64(inputs)
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w))
+    compare(w, [to_np(o), to_np(to), to_np(lse)], ref, label="strided")
