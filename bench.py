@@ -1,0 +1,201 @@
+"""Benchmark of the custom-mask attention-JVP forward on one MI355X.
+
+One step = one attn_jvp_fwd launch over the whole workload (all heads and
+rows): scores, score tangents, online softmax, the three value products and the
+epilogue.  Inputs are seeded synthetic tensors already resident in HBM.
+
+Metric: TFLOP/s of unmasked work, counting 12*d FLOP per allowed
+(batch, head, query, key) pair (QK^T 2d, tQK^T + QtK^T 4d, P V 2d, P tV 2d,
+(P.tS) V 2d), as a fraction of the MI355X dense bf16 MFMA peak.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", "attn_jvp_fwd.hip")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the rocprofv3 counter runs recorded under
+    profiles/, or None if they were taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, heads: int):
+    """Times the fp64 oracle (as it stands) on the first `heads` heads of batch 0."""
+    import numpy as np
+
+    from oracle import MaskLayout, attn_jvp_ref, unmasked_pairs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
+    except Exception:  # pragma: no cover - reporting only
+        threads, blas = os.cpu_count(), "unknown"
+    m = MaskLayout(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk)
+    import torch
+
+    x = {n: t[:1, :heads].to(torch.float64).numpy() for n, t in inputs.items()}
+    t0 = time.perf_counter()
+    attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], m, scale=w.scale)
+    dt = time.perf_counter() - t0
+    flop = 12.0 * w.head_dim * unmasked_pairs(m) * heads
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle ({blas}), batch 0, {heads} of {w.heads} heads, all {w.seq_len} rows; "
+                      f"{dt:.1f} s for {flop:.3e} FLOP",
+            "seconds": round(dt, 2),
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the c3-3 Wan2.1-1.3B shape)")
+    ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads timed for the oracle baseline (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import attention_jvp_causal_amd as aj
+    from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    inputs = make_inputs(w)
+    dev = {n: t.to("cuda:0") for n, t in inputs.items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    pairs = desc.unmasked_pairs * w.batch * w.heads
+    flop = 12.0 * w.head_dim * pairs
+    out_dtype = {None: None, "bf16": torch.bfloat16, "f32": torch.float32}[args.out_dtype]
+    B, H, L, D = w.shape
+    odt = out_dtype or dev["q"].dtype
+    outs = (torch.empty((B, H, L, D), dtype=odt, device="cuda:0"),
+            torch.empty((B, H, L, D), dtype=odt, device="cuda:0"),
+            torch.empty((B, H, L), dtype=torch.float32, device="cuda:0"))
+    args_ = [dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")]
+
+    def step():
+        aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()  # the binding launches on this stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    traffic = measured_traffic(w.name)
+    in_bytes = 6 * B * H * L * D * inputs["q"].element_size()
+    out_bytes = 2 * B * H * L * D * odt.itemsize + B * H * L * 4
+
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline(w, inputs, min(args.cpu_heads, w.heads))
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. Gaussian Q, K, V and tangents, Wan2.1 480p latent shapes)",
+        "config": {
+            "workload": w.name,
+            "batch": B, "heads": H, "seq_len": L, "head_dim": D,
+            "mask": f"{w.mask_kind} frames={w.num_frames} tokens_per_frame={w.frame_tokens} "
+                    f"frames_per_chunk={w.frames_per_chunk}",
+            "unmasked_pairs": pairs,
+            "flop_per_step": flop,
+            "out_dtype": str(odt).replace("torch.", ""),
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "attn_jvp_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_jvp_fwd_f32_kernel",
+            "launch_ms_avg": round(avg_ms, 4),
+            "launch_ms_min": round(launch_ms[0], 4),
+            "algorithmic_hbm_bytes": in_bytes + out_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
