@@ -32,6 +32,12 @@ def compile_flags():
         # packed fp32 instructions stay off: plain float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
+        # kernels never produce NaN (masked scores are -inf and guarded), so
+        # fmaxf needs no NaN canonicalisation
+        "-fno-honor-nans",
+        # MFMA accumulators in VGPRs: the online-softmax rescale multiplies them
+        # with VALU ops, which cannot address AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         f"-I{os.path.join(ROOT, 'include')}",
     ]
 
