@@ -14,12 +14,13 @@
 // l+32 share a row and split its keys), so the softmax statistics are per lane
 // and the accumulator registers feed the next MFMA as its B operand without any
 // data movement:
-//   O^T  += V^T  P~^T        A^T += V^T (P~ . tS)^T        B^T += tV^T P~^T
-// V and tV are therefore staged transposed (d-major) in LDS.
+//   O~^T += V^T P~^T        (A + B)^T += V^T (P~ . tS)^T + tV^T P~^T
+// V and tV are read from LDS with transpose reads.
 //
 // Online softmax (fp32, per row): running max m, denominator l, and the JVP
 // accumulators A = sum p~ ts v, B = sum p~ tv, mu = sum p~ ts share one rescale
-// factor with O.  Finally O = O~/l and tO = (A + B - mu O)/l (Eq. 45).
+// factor with O~.  Only A + B enters the result, so A and B are accumulated
+// in one register set.  Finally O = O~/l and tO = (A + B - mu O)/l (Eq. 45).
 // Rescaling is lazy: the reference max only moves when a row's max grows by
 // more than 2^8, which is exact in real arithmetic (all terms of a row share
 // the reference) and bounds p~ by 256.

@@ -1,0 +1,43 @@
+"""Build-time guards on the generated gfx950 code (CPU only: hipcc cross-compiles).
+
+The key-tile DMA is issued from a small asm block that sets m0; that is safe
+only while the compiler itself keeps nothing in m0 in these kernels.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from attention_jvp_causal_amd import build as B
+
+
+def _device_asm(tmp_path):
+    out = tmp_path / "k.s"
+    cmd = [B.hipcc(), *B.compile_flags(), "-x", "hip", "-S", "--cuda-device-only",
+           os.path.join(B.CSRC, "attn_jvp_fwd.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_m0_only_used_by_the_dma_asm_blocks(tmp_path):
+    asm = _device_asm(tmp_path)
+    kernels = re.findall(r"^(_ZN2aj\w+kernel\w+):", asm, flags=re.M)
+    assert any("bf16" in k for k in kernels) and any("f32" in k for k in kernels)
+    inside = False
+    outside_uses = []
+    for line in asm.splitlines():
+        if "ASMSTART" in line:
+            inside = True
+        elif "ASMEND" in line:
+            inside = False
+        elif re.search(r"\bm0\b", line.split(";")[0]) and not inside:
+            outside_uses.append(line.strip())
+    assert not outside_uses, outside_uses[:5]
+    # no private (scratch) segment in the hot kernels
+    for spill in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm):
+        assert int(spill) == 0
