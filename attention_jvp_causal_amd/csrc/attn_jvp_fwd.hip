@@ -60,13 +60,42 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_
 // ---------------------------------------------------------------------------
 // bf16 inputs
 // ---------------------------------------------------------------------------
+//
+// Two wave shapes share one streaming scheme; the launcher picks by head_dim.
+//
+// * q16 (head_dim 128): a workgroup is 8 waves (two per SIMD); wave w owns
+//   query rows 16w .. 16w+15 of the 128-row tile.  With 16 rows per wave the
+//   row state (Q, tQ, O~, A+B, scores) fits in 256 registers, so each SIMD
+//   runs two waves and the hardware overlaps one wave's softmax and LDS
+//   latency with the other wave's MFMAs.  MFMA v_mfma_f32_16x16x32_bf16 on
+//   transposed scores S^T = K Q^T: lane l = 16g + j holds keys 4g + r
+//   (r = 0..3) of each 16-key block for query row j, i.e. one query per
+//   16-lane column with its keys split over the four groups g.  Two 16-key
+//   blocks form the 8 k-slots of a value MFMA's B operand, so the score
+//   accumulators feed O~^T += V^T P~^T directly.
+// * q32 (head_dim 64): a workgroup is 4 waves of 32 rows each, two
+//   workgroups per CU; MFMA v_mfma_f32_32x32x16_bf16 on S^T, lanes l and
+//   l+32 share one query row.  At d = 64 the softmax's vector work matches
+//   the matrix work per element, and the larger waves amortise the per-tile
+//   fixed costs better.
+//
+// Both stream key tiles of 64 keys (K, tK, V, tV rows and, for partial
+// tiles, the 128 per-row key bitmasks) by direct buffer -> LDS DMA into a
+// double buffer: tile t+1 loads while tile t computes.  V and tV are read with
+// gfx950's LDS transpose read.  Rows are unpadded; 16-byte chunk c of row r is
+// stored at position c ^ swz(r), chosen per shape so that every operand read
+// is free of conflicts on the 64-bank LDS:
+//   q16, D = 128: swz(r) = 2 (r % 8) + (r / 8) % 2         (K: one chunk of 16
+//   q16, D =  64: swz(r) = 2 ((r / 2) % 4) + (r / 8) % 2    rows per 16 lanes;
+//                                                           V: two chunks of 8
+//                                                           rows per 32 lanes)
+//   q32, D = 128: swz(r) = 4 (r % 4) + (r / 4) % 4         (K: one chunk of 16
+//   q32, D =  64: swz(r) = 4 ((r / 2) % 2) + (r / 4) % 4    rows; V: four
+//                                                           chunks of 4 rows)
 
-// LDS holds two buffers of {K, tK, V, tV} key tiles, each [BN][D] bf16 with
-// unpadded rows.  The 16-byte chunks of row r are stored XOR-swizzled:
-// logical chunk c sits at position c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2.
-// This makes both read patterns bank-conflict free: ds_read_b128 of one chunk
-// from 8 consecutive rows (K operands), and the transpose reads of V, which
-// take two adjacent chunks from 4 consecutive rows.
+constexpr int kWavesQ16 = 8;
+constexpr int kWavesQ32 = 4;
+
 template <int D>
 struct Bf16Lds {
   static constexpr int TILE = BN * D;  // elements per tensor tile
@@ -74,41 +103,31 @@ struct Bf16Lds {
   uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz_q16(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_q32(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer resource: 32-bit data, no swizzle
 
-// Per-lane byte offsets (inside one key tile of one tensor) of the 16-byte
-// chunks this lane moves with direct buffer -> LDS loads.  Wave instruction
-// i fills 1 KB block blk = wave + 4i of the tile: lane l writes LDS chunk
-// blk*64 + l, i.e. row r = chunk / CH at swizzled position p, so it fetches
-// logical chunk p ^ swz(r) of row r.
-template <int D>
-struct TileLoadPlan {
-  static constexpr int CH = D / 8;                       // 16-byte chunks per row
-  static constexpr int NI = (BN * CH) / (64 * NWAVES);   // wave instructions per tensor
-  uint32_t voff[NI];
-  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int ci = (wave + NWAVES * i) * 64 + lane;
-      const int r = ci / CH, p = ci % CH;
-      voff[i] = uint32_t(r * sl * 2 + ((p ^ swz(r)) << 4));
-    }
-  }
-};
-
 // One direct buffer -> LDS load of 16 bytes per lane: lane l's chunk lands at
-// LDS byte address lds_base + 16 l.  Written as inline asm so that the compiler
-// does not track it: the kernel waits for these loads itself (wait_vmcnt)
-// right before the barrier that publishes the buffer, instead of the
-// compiler's conservative wait for every load in flight into any buffer.
-// The instruction has no register results; it only writes LDS.
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+// LDS byte address lds_base + 16 l.  Written as inline asm so that the
+// compiler does not track it: the kernel waits for these loads itself
+// (wait_vmcnt) right before the barrier that publishes a buffer, instead of
+// the compiler's conservative wait for every load in flight into any buffer.
+// The instruction has no register results; it only writes LDS.  m0 is set
+// here and used by nothing else in these kernels (checked by a build test).
 __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, uint32_t voffset, i32x4_t rsrc) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -119,49 +138,60 @@ __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, uint32_t voffset, 
       : "memory", "m0");
 }
 
-// Issues the loads of key tile [key0, key0 + BN) of the four tensors into one
-// LDS buffer (dst = its K, tK, V, tV tiles).  Returns immediately; completion
-// is tracked by vmcnt.  The buffer resource starts at row key0 and ends at row
-// L, so rows past the end read as zero.
-template <int D>
-__device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<D>& plan,
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4_t rs;
+  rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  rs.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);  // stride 0
+  rs.z = __builtin_amdgcn_readfirstlane(nbytes);
+  rs.w = kRsrcWord3;
+  return rs;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// Per-lane byte offsets (inside one key tile of one tensor) of the 16-byte
+// chunks this lane moves.  Wave instruction i fills 1 KB block blk = wave +
+// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. row r = chunk /
+// CH at swizzled position p, so it fetches logical chunk p ^ swz(r) of row r.
+template <int NW, int D>
+struct TileLoadPlan {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int NI = (BN * CH) / (64 * NW);   // wave instructions per tensor
+  static constexpr int PER_TILE = 4 * NI;            // DMA instructions per wave per tile
+  uint32_t voff[NI];
+  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ci = (wave + NW * i) * 64 + lane;
+      const int r = ci / CH, p = ci % CH;
+      voff[i] = uint32_t(r * sl * 2 + ((p ^ swz(r)) << 4));
+    }
+  }
+};
+
+// Issues the DMA of key tile [key0, key0 + BN) of the four tensors into one
+// LDS buffer.  Returns immediately; completion is tracked by vmcnt.  The
+// buffer resource ends at row L, so rows past the end read as zero.
+template <int NW, int D>
+__device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* const src[4], int64_t sl, int key0, int L,
                                                  int wave) {
   const int nrec = int((int64_t)(L - key0) * sl * 2);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint64_t base = (uint64_t)(src[t] + (int64_t)key0 * sl);
-    i32x4_t rs;
-    rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-    rs.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32) & 0xffff);  // stride 0
-    rs.z = __builtin_amdgcn_readfirstlane(nrec);
-    rs.w = kRsrcWord3;
+    const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
 #pragma unroll
-    for (int i = 0; i < TileLoadPlan<D>::NI; ++i) {
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(dst[t] + (wave + NWAVES * i) * 512));
-      lds_dma_16(lds, plan.voff[i], rs);
-    }
+    for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+      lds_dma_16(lds_addr(dst[t] + (wave + NW * i) * 512), plan.voff[i], rs);
   }
 }
 
-// Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx into
-// LDS: one 16-byte chunk (two rows) per lane.
+// Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx.
 __device__ __forceinline__ void issue_bits_load(uint64_t* dst, const uint64_t* bits, int pidx, int lane) {
-  const uint64_t base = (uint64_t)(bits + (int64_t)pidx * BM);
-  i32x4_t rs;
-  rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-  rs.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32) & 0xffff);
-  rs.z = BM * 8;
-  rs.w = kRsrcWord3;
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)dst);
-  lds_dma_16(lds, uint32_t(lane) * 16u, rs);
-}
-
-template <int D>
-constexpr int loads_per_tile() {
-  return 4 * (BN * (D / 8)) / (64 * NWAVES);
+  lds_dma_16(lds_addr(dst), uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -172,13 +202,282 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// max over lanes l and l^32 (the two halves of one q32 query row) without
+// the LDS pipe: v_permlane32_swap exchanges the upper half of one operand with
+// the lower half of the other.
+__device__ __forceinline__ float row_max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 of one q16 query row
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// ---- q16 shape --------------------------------------------------------------
+
 template <int D, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
-void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ16, 64 * kWavesQ16), amdgpu_waves_per_eu(2, 2)))
+void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
+  constexpr int NKS = D / 32;  // MFMA k-steps over d for the score products
+  constexpr int NDB = D / 16;  // 16-row blocks of d for the value products
+  constexpr int NLOADS = TileLoadPlan<kWavesQ16, D>::PER_TILE;
+  using Lds = Bf16Lds<D>;
+  __shared__ __attribute__((aligned(1024))) Lds s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int qt = a.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
+  const uint16_t* __restrict__ tQg = (const uint16_t*)a.tq + in_off;
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, (const uint16_t*)a.tk + in_off,
+                                  (const uint16_t*)a.v + in_off, (const uint16_t*)a.tv + in_off};
+  const int q_row = qt * BM + wave * 16 + j16;
+
+  // Q and tQ of this lane's query row, as B operands: k-step ks holds
+  // d = 32ks + 8g .. 32ks + 8g + 7.
+  bf16x8_t Qr[NKS], tQr[NKS];
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int64_t off = q_row * a.isl + ks * 32 + 8 * g;
+      Qr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
+      tQr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
+    }
+  }
+  // Q and tQ have landed before any DMA is in flight: the compiler tracks no
+  // load inside the tile loop.
+  wait_vmcnt<0>();
+
+  const TileLoadPlan<kWavesQ16, D> plan(a.isl, wave, lane, swz_q16<D>);
+  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  int e = e0, kt = 0;
+  Entry en = {0, 0, -1, 0};
+  if (e < e1) {
+    en = a.entries[e];
+    kt = en.kt0;
+    issue_tile_loads<kWavesQ16, D>(s.t[0], plan, src, a.isl, kt * BN, L, wave);
+    if (en.pidx >= 0 && wave == 0) issue_bits_load(s.bits[0], a.bits, en.pidx, lane);
+  }
+
+  f32x4_t Oacc[NDB], ABacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
+  float m_run = -INFINITY;            // reference max (log2 units, scale folded in)
+  float l_part = 0.f, mu_part = 0.f;  // this lane's share of the row sums
+  const float sl2 = a.scale_log2, c = a.scale;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Per-lane LDS offsets (elements) that do not depend on the tile.
+  // K operand of 16-key block kb, k-step ks: row 16kb + j16 (swz(16kb + j16)
+  // == swz(j16)), logical chunk 4ks + g.
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
+  // V^T operand (transpose read) of value k-step p (keys 32p .. 32p+31), d
+  // block db: lane j16 of group g names key 32p + 4g + j16/4 (+16 for the
+  // second read) and d = 16db + 4(j16%4), i.e. logical chunk 2db + (j16%4)/2,
+  // half j16 % 2.  swz depends on the row mod 16, which 32p and 16 keep.
+  const int vrow = 4 * g + (j16 >> 2);
+  int voff[2][NDB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow + 16 * h;
+      const int chunk = 2 * db + ((j16 & 3) >> 1);
+      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
+    }
+
+  int buf = 0;
+  while (e < e1) {
+    // next key tile into the other buffer while this one is computed
+    int e_n = e, kt_n = kt + 1;
+    Entry en_n = en;
+    if (kt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.entries[e_n];
+        kt_n = en_n.kt0;
+      }
+    }
+    const bool has_next = e_n < e1;
+    if (has_next) {
+      issue_tile_loads<kWavesQ16, D>(s.t[buf ^ 1], plan, src, a.isl, kt_n * BN, L, wave);
+      if (en_n.pidx >= 0 && wave == 0) {
+        issue_bits_load(s.bits[buf ^ 1], a.bits, en_n.pidx, lane);
+        wait_vmcnt<NLOADS + 1>();
+      } else {
+        wait_vmcnt<NLOADS>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const uint16_t* Kt = s.t[buf][0];
+    const uint16_t* tKt = s.t[buf][1];
+    const uint16_t* Vt = s.t[buf][2];
+    const uint16_t* tVt = s.t[buf][3];
+
+    // ---- scores and score tangents of the 64-key tile (transposed) ----
+    f32x4_t S[4], TS[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[kb][r] = TS[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int off = kb * 16 * D + koff[ks];
+        const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
+        const bf16x8_t tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
+        S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, Qr[ks], S[kb], 0, 0, 0);
+        TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tkop, Qr[ks], TS[kb], 0, 0, 0);
+        TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, tQr[ks], TS[kb], 0, 0, 0);
+      }
+    }
+    // lane holds keys 16kb + 4g + r of query row j16
+
+    // ---- partial tile: masked-out pairs take no part (select; no tangent) ----
+    if (en.pidx >= 0) {
+      const uint64_t bits = s.bits[buf][wave * 16 + j16] >> (4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (bits >> (16 * kb + r)) & 1ull;
+          S[kb][r] = ok ? S[kb][r] : -INFINITY;
+          TS[kb][r] = ok ? TS[kb][r] : 0.f;
+        }
+    }
+
+    // ---- online softmax with lazy rescale ----
+    float mx = S[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = row4_max(mx);
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const bool need = m_new > m_run + kLazyRescaleLog2;
+    if (__any(need)) {
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = need ? m_new : m_run;
+      l_part *= alpha;
+      mu_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Oacc[db][r] *= alpha;
+          ABacc[db][r] *= alpha;
+        }
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+
+    // p~ = exp2(c log2e s - m); u = p~ * (c ts).  Both rounded to bf16 once;
+    // l and mu are summed from the rounded values.  Value k-step p takes
+    // blocks 2p (slots 0..3) and 2p+1 (slots 4..7).
+    bf16x8_t P[2], U[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        f32x2_t p, u;
+        p.x = fast_exp2(__builtin_fmaf(S[kb][r], sl2, -m_use));
+        p.y = fast_exp2(__builtin_fmaf(S[kb][r + 1], sl2, -m_use));
+        u.x = p.x * (TS[kb][r] * c);
+        u.y = p.y * (TS[kb][r + 1] * c);
+        const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
+        const bf16x2_t ub = __builtin_convertvector(u, bf16x2_t);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
+        mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+        const int slot = 4 * (kb & 1) + r;
+        P[kb >> 1][slot] = pb.x;
+        P[kb >> 1][slot + 1] = pb.y;
+        U[kb >> 1][slot] = ub.x;
+        U[kb >> 1][slot + 1] = ub.y;
+      }
+
+    // ---- value products (transposed: rows = d, cols = queries) ----
+    //   O~ += V^T P~^T ;  (A + B) += V^T U^T + tV^T P~^T
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int off_a = 32 * p * D + voff[0][db];
+        const int off_b = 32 * p * D + voff[1][db];
+        const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
+        const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
+        const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+        Oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, P[p], Oacc[db], 0, 0, 0);
+        ABacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, U[p], ABacc[db], 0, 0, 0);
+        ABacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tvop, P[p], ABacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+    e = e_n;
+    kt = kt_n;
+    en = en_n;
+    buf ^= 1;
+  }
+
+  // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
+  const float l_tot = row4_sum(l_part);
+  const float mu_tot = row4_sum(mu_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_row < L) {
+    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = db * 16 + 4 * g;
+      f32x4_t ov, tv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float o = Oacc[db][r] * inv;
+        ov[r] = o;
+        tv[r] = (ABacc[db][r] - mu_tot * o) * inv;
+      }
+      if constexpr (OUT_F32) {
+        *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
+        *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+      } else {
+        *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
+        *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
+      }
+    }
+    if (g == 0)
+      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---- q32 shape --------------------------------------------------------------
+
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32), amdgpu_waves_per_eu(2, 2)))
+void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
-  constexpr int CH = D / 8;
-  constexpr int NLOADS = loads_per_tile<D>();
+  constexpr int NLOADS = TileLoadPlan<kWavesQ32, D>::PER_TILE;
   __shared__ __attribute__((aligned(1024))) Bf16Lds<D> s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -195,14 +494,14 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
   const int q_row = qt * BM + wave * 32 + l32;
 
   // first key tile in flight before the prologue
-  const TileLoadPlan<D> plan(a.isl, wave, lane);
+  const TileLoadPlan<kWavesQ32, D> plan(a.isl, wave, lane, swz_q32<D>);
   const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
     en = a.entries[e];
     kt = en.kt0;
-    issue_tile_loads<D>(s.t[0], plan, src, a.isl, kt * BN, L, wave);
+    issue_tile_loads<kWavesQ32, D>(s.t[0], plan, src, a.isl, kt * BN, L, wave);
     if (en.pidx >= 0 && wave == 0) issue_bits_load(s.bits[0], a.bits, en.pidx, lane);
   }
 
@@ -232,23 +531,20 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
   const float sl2 = a.scale_log2, c = a.scale;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Per-lane LDS offsets (elements) that do not depend on the tile; the rest
-  // of every read offset is a compile-time constant.
-  // K operand of 32-key block kb, k-step kk: row kb*32 + l32, logical chunk
-  // 2kk + hi.  swz(kb*32 + l32) == swz(l32), and chunk 2kk + hi differs from
-  // 2(kk%4) + hi only in bit 3, which the swizzle never touches.
-  int koff[4];
+  int koff[NKK];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) koff[q] = l32 * D + (((2 * q + hi) ^ swz(l32)) << 3);
-  // V^T operand (transpose read): within each 16-lane group g, lane j names
-  // key 4hi + j/4 (+8 for the second read) and d = 32db + 16(g%2) + 4(j%4);
-  // logical chunk 4db + c0 with c0 = d/8 % 4, swizzle of the row is swz(vrow0).
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * D + (((2 * kk + hi) ^ swz_q32<D>(l32)) << 3);
   const int g = lane >> 4, j = lane & 15;
   const int vrow0 = 4 * hi + (j >> 2);
   const int vd0 = 16 * (g & 1) + 4 * (j & 3);
-  int voff2[2];
+  int voff[2][NDB];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) voff2[q] = vrow0 * D + (((4 * q + (vd0 >> 3)) ^ swz(vrow0)) << 3) + (vd0 & 7);
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow0 + 8 * h8;
+      voff[h8][db] = row * D + (((4 * db + (vd0 >> 3)) ^ swz_q32<D>(row)) << 3) + (vd0 & 7);
+    }
 
   int buf = 0;
   while (e < e1) {
@@ -264,7 +560,7 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
     }
     const bool has_next = e_n < e1;
     if (has_next) {
-      issue_tile_loads<D>(s.t[buf ^ 1], plan, src, a.isl, kt_n * BN, L, wave);
+      issue_tile_loads<kWavesQ32, D>(s.t[buf ^ 1], plan, src, a.isl, kt_n * BN, L, wave);
       // wait for all but the next tile's loads (issued last)
       if (en_n.pidx >= 0 && wave == 0) {
         issue_bits_load(s.bits[buf ^ 1], a.bits, en_n.pidx, lane);
@@ -290,7 +586,7 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) S[r] = TS[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int off = kb * 32 * D + (kk >> 2) * 64 + koff[kk & 3];
+        const int off = kb * 32 * D + koff[kk];
         const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
         const bf16x8_t tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
@@ -314,7 +610,7 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
       float mx = S[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-      mx = fmaxf(mx, wave_xor32(mx));
+      mx = row_max_halves(mx);
       const float m_new = fmaxf(m_run, mx * sl2);
       const bool need = m_new > m_run + kLazyRescaleLog2;
       if (__any(need)) {
@@ -362,8 +658,8 @@ void attn_jvp_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           // keys kb*32 + 16st + vrow0 (slots 0..3) and 8 further (slots 4..7)
-          const int off_a = (kb * 32 + 16 * st) * D + (db >> 1) * 64 + voff2[db & 1];
-          const int off_b = off_a + 8 * D;
+          const int off_a = (kb * 32 + 16 * st) * D + voff[0][db];
+          const int off_b = (kb * 32 + 16 * st) * D + voff[1][db];
           const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
           const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
           const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
@@ -601,18 +897,19 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
 int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, hipStream_t stream) {
   const int64_t grid64 = int64_t(a.n_tasks) * a.B * a.H;
   if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
-  const dim3 grid((unsigned)grid64), block(NTHREADS);
+  const dim3 grid((unsigned)grid64);
+  const dim3 b16(64 * kWavesQ16), b32(64 * kWavesQ32), b_f32(NTHREADS);
   if (in_dtype == AJ_BF16) {
     if (out_dtype == AJ_BF16) {
-      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false>), grid, b16, 0, stream, a);
+      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false>), grid, b32, 0, stream, a);
     } else {
-      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true>), grid, b16, 0, stream, a);
+      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true>), grid, b32, 0, stream, a);
     }
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<128>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<64>), grid, block, 0, stream, a);
+    if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<128>), grid, b_f32, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<64>), grid, b_f32, 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? AJ_OK : AJ_EHIP;
 }
