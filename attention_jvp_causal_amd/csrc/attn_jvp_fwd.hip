@@ -337,20 +337,28 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     const uint16_t* tVt = s.t[buf][3];
 
     // ---- scores and score tangents of the 64-key tile (transposed) ----
+    // k-step outer, key block inner: four independent accumulator chains per
+    // operand, so consecutive MFMAs never depend on each other.
     f32x4_t S[4], TS[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[kb][r] = TS[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8_t kop[4], tkop[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
         const int off = kb * 16 * D + koff[ks];
-        const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
-        const bf16x8_t tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
-        S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, Qr[ks], S[kb], 0, 0, 0);
-        TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tkop, Qr[ks], TS[kb], 0, 0, 0);
-        TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, tQr[ks], TS[kb], 0, 0, 0);
+        kop[kb] = as_bf16x8(*(const u32x4_t*)(Kt + off));
+        tkop[kb] = as_bf16x8(*(const u32x4_t*)(tKt + off));
       }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], Qr[ks], S[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tkop[kb], Qr[ks], TS[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], tQr[ks], TS[kb], 0, 0, 0);
     }
     // lane holds keys 16kb + 4g + r of query row j16
 
@@ -417,21 +425,30 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
 
     // ---- value products (transposed: rows = d, cols = queries) ----
     //   O~ += V^T P~^T ;  (A + B) += V^T U^T + tV^T P~^T
+    // four d blocks at a time: independent accumulator chains between the
+    // dependent (A + B) updates
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int off_a = 32 * p * D + voff[0][db];
-        const int off_b = 32 * p * D + voff[1][db];
-        const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
-        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
-        const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
-        const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
-        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
-        Oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, P[p], Oacc[db], 0, 0, 0);
-        ABacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, U[p], ABacc[db], 0, 0, 0);
-        ABacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tvop, P[p], ABacc[db], 0, 0, 0);
+      for (int d4 = 0; d4 < NDB; d4 += 4) {
+        bf16x8_t vop[4], tvop[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int off_a = 32 * p * D + voff[0][d4 + i];
+          const int off_b = 32 * p * D + voff[1][d4 + i];
+          const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
+          const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
+          const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
+          const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+          vop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+          tvop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Oacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[i], P[p], Oacc[d4 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[i], U[p], ABacc[d4 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tvop[i], P[p], ABacc[d4 + i], 0, 0, 0);
       }
     }
     __syncthreads();  // every wave is done with this buffer before it is refilled
