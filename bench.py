@@ -43,6 +43,14 @@ def kernel_sha() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
+def kernel_name(dtype: str, head_dim: int, out_f32: bool) -> str:
+    """Name of the kernel instance the library launches for this configuration."""
+    if dtype == "f32":
+        return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
+    kind = "q16" if head_dim == 128 else "q32"
+    return f"attn_jvp_fwd_bf16_{kind}_kernel<{head_dim}, {'true' if out_f32 else 'false'}>"
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the rocprofv3 counter runs recorded under
     profiles/, or None if they were taken on a different kernel source."""
@@ -54,6 +62,59 @@ def measured_traffic(workload: str):
     if rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("bytes_per_launch")
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int, command: str) -> dict:
+    """Builds profiles/traffic_<workload>.json from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE) of this script with --calib-copy-mib.
+
+    Both counters are in KiB per dispatch.  Each is scaled by the factor that
+    makes the device copy of known size read (write) exactly its size, and the
+    kernel's dispatches are averaged."""
+    import csv
+    from collections import defaultdict
+
+    from attention_jvp_causal_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[workload]
+    kname = kernel_name(w.dtype, w.head_dim, False)
+    kname_sym = kname.split("<")[0]
+
+    def per_dispatch(path, counter):
+        acc = defaultdict(float)
+        names = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        copy = [v for d, v in acc.items() if "copyBuffer" in names[d]]
+        kern = [v for d, v in acc.items() if kname_sym in names[d]]
+        if len(copy) != 1 or not kern:
+            raise SystemExit(f"{path}: expected one copy dispatch and >=1 {kname_sym} dispatch")
+        return copy[0], sum(kern) / len(kern), len(kern)
+
+    calib = calib_mib * (1 << 20)
+    fc, fk, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wc, wk, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    ff, wf = calib / (fc * 1024), calib / (wc * 1024)
+    rec = {
+        "workload": workload,
+        "kernel": kname,
+        "kernel_sha": kernel_sha(),
+        "fetch_size_kib_per_dispatch": round(fk, 1),
+        "write_size_kib_per_dispatch": round(wk, 1),
+        "dispatches_averaged": [nf, nw],
+        "copy_calibration": {"bytes": calib, "fetch_size_kib": fc, "write_size_kib": wc,
+                             "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+        "bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf)),
+        "command": command,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def cpu_baseline(w, inputs, heads: int):
@@ -95,7 +156,19 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads timed for the oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 counter_collection.csv "
+                         "files (FETCH_SIZE run, WRITE_SIZE run) and exit; needs no GPU")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD
+
+        wl = args.workload or BENCH_WORKLOAD
+        cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+               f"--workload {wl} --steps 3 --warmup 1 --cpu-heads 0 --calib-copy-mib {args.calib_copy_mib or 1024}")
+        print(json.dumps(record_traffic(wl, *args.record_traffic, args.calib_copy_mib or 1024, cmd)))
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not part of it",
@@ -193,7 +266,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": "attn_jvp_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_jvp_fwd_f32_kernel",
+            "kernel": kernel_name(w.dtype, D, odt == torch.float32),
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,
