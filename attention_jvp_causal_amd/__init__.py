@@ -74,9 +74,15 @@ def lib() -> ctypes.CDLL:
     L.attn_jvp_mask_desc_tile_kind.argtypes = [pdesc, i32, i32, ctypes.POINTER(i32)]
     L.attn_jvp_mask_desc_row_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     L.attn_jvp_mask_desc_free.argtypes, L.attn_jvp_mask_desc_free.restype = [pdesc], None
+    L.attn_jvp_mask_desc_tangent_free.argtypes = [pdesc, P, i32, ctypes.POINTER(pdesc)]
+    L.attn_jvp_mask_desc_work.argtypes = [pdesc, ctypes.POINTER(i64)]
+    L.attn_jvp_mask_desc_tile_variant.argtypes = [pdesc, i32, i32, ctypes.POINTER(i32)]
     L.attn_jvp_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
+    L.attn_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, pdesc, f32, P, P, P]
     for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
-               "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd"):
+               "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
+               "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
+               "attn_fwd"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -132,6 +138,19 @@ class MaskDesc:
                "attn_jvp_mask_desc_tile_kind")
         return k.value
 
+    def tile_variant(self, q_tile: int, k_tile: int) -> int:
+        """-1 skipped, 0 all JVP products, 1 keys tangent-free, 3 all tangent-free."""
+        k = ctypes.c_int32()
+        _check(lib().attn_jvp_mask_desc_tile_variant(self.handle, q_tile, k_tile, ctypes.byref(k)),
+               "attn_jvp_mask_desc_tile_variant")
+        return k.value
+
+    def work(self) -> Tuple[int, int, int]:
+        """Allowed pairs per (batch, head) in tiles doing 12 D, 8 D and 4 D FLOP per pair."""
+        w = (ctypes.c_int64 * 3)()
+        _check(lib().attn_jvp_mask_desc_work(self.handle, w), "attn_jvp_mask_desc_work")
+        return int(w[0]), int(w[1]), int(w[2])
+
     def row_bits(self, q_tile: int, k_tile: int, row: int) -> int:
         b = ctypes.c_uint64()
         _check(lib().attn_jvp_mask_desc_row_bits(self.handle, q_tile, k_tile, row, ctypes.byref(b)),
@@ -177,23 +196,27 @@ def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], 
     return MaskDesc(out.value, head_dim, dt)
 
 
+def attn_jvp_mask_desc_tangent_free(base: MaskDesc, ranges: Sequence[Sequence[int]]) -> MaskDesc:
+    """Descriptor with base's mask that declares tq, tk, tv zero on the token
+    ranges [t0, t1) (see the header); the JVP then skips the zero products."""
+    flat = [int(x) for r in ranges for x in r]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    out = ctypes.c_void_p()
+    _check(lib().attn_jvp_mask_desc_tangent_free(base.handle, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 2,
+                                                 ctypes.byref(out)),
+           "attn_jvp_mask_desc_tangent_free")
+    return MaskDesc(out.value, base.head_dim, base.dtype)
+
+
 def attn_jvp_mask_desc_free(handle) -> None:
     lib().attn_jvp_mask_desc_free(handle)
 
 
-def attn_jvp_fwd(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = None,
-                 out_dtype=None, out: Optional[Tuple] = None, stream=None):
-    """O, tO, lse of masked attention and its JVP on the GPU (one kernel launch).
-
-    q, k, v, tq, tk, tv: CUDA/HIP tensors [B, H, L, D] (bf16 or fp32) with the
-    D axis contiguous and identical strides.  Returns (o, to, lse): o and to
-    [B, H, L, D] in ``out_dtype`` (default: the input dtype), lse [B, H, L]
-    float32.  ``out`` may pass preallocated (o, to, lse).
-    """
+def _prepare(ins, out_dtype, scale, out, n_out_tensors):
+    """Checks the inputs and builds (shape struct, outputs, scale)."""
     import torch
 
-    ins = (q, k, v, tq, tk, tv)
-    x0 = q
+    x0 = ins[0]
     if any(t.device != x0.device for t in ins) or x0.device.type != "cuda":
         raise ValueError("all inputs must be on the same GPU device")
     if any(t.dtype != x0.dtype for t in ins) or any(t.shape != x0.shape for t in ins):
@@ -213,29 +236,67 @@ def attn_jvp_fwd(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = N
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        o = torch.empty((B, H, L, D), dtype=odt, device=x0.device)
-        to = torch.empty_like(o)
+        outs = [torch.empty((B, H, L, D), dtype=odt, device=x0.device) for _ in range(n_out_tensors)]
         lse = torch.empty((B, H, L), dtype=torch.float32, device=x0.device)
     else:
-        o, to, lse = out
-        if o.shape != x0.shape or to.shape != x0.shape or o.dtype != odt or to.dtype != odt:
-            raise ValueError("preallocated o / to have the wrong shape or dtype")
-        if o.stride() != to.stride() or o.stride(3) != 1:
-            raise ValueError("preallocated o / to must share strides with D contiguous")
+        *outs, lse = out
+        if len(outs) != n_out_tensors:
+            raise ValueError(f"out must hold {n_out_tensors + 1} tensors")
+        for o in outs:
+            if o.shape != x0.shape or o.dtype != odt:
+                raise ValueError("preallocated outputs have the wrong shape or dtype")
+            if o.stride() != outs[0].stride() or o.stride(3) != 1:
+                raise ValueError("preallocated outputs must share strides with D contiguous")
         if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError("preallocated lse must be a contiguous float32 [B, H, L] tensor")
-    sh = aj_shape(B, H, L, D, in_dt, out_dt, *x0.stride()[:3], *o.stride()[:3])
+    sh = aj_shape(B, H, L, D, in_dt, out_dt, *x0.stride()[:3], *outs[0].stride()[:3])
+    return sh, outs, lse, float(scale)
+
+
+def attn_jvp_fwd(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = None,
+                 out_dtype=None, out: Optional[Tuple] = None, stream=None):
+    """O, tO, lse of masked attention and its JVP on the GPU (one kernel launch).
+
+    q, k, v, tq, tk, tv: CUDA/HIP tensors [B, H, L, D] (bf16 or fp32) with the
+    D axis contiguous and identical strides.  Returns (o, to, lse): o and to
+    [B, H, L, D] in ``out_dtype`` (default: the input dtype), lse [B, H, L]
+    float32.  ``out`` may pass preallocated (o, to, lse).
+    """
+    import torch
+
+    ins = (q, k, v, tq, tk, tv)
+    sh, (o, to), lse, scale = _prepare(ins, out_dtype, scale, out, 2)
     if stream is None:
-        stream = torch.cuda.current_stream(x0.device).cuda_stream
-    with torch.cuda.device(x0.device):
-        st = lib().attn_jvp_fwd(ctypes.byref(sh), *(t.data_ptr() for t in ins), mask.handle, float(scale),
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_jvp_fwd(ctypes.byref(sh), *(t.data_ptr() for t in ins), mask.handle, scale,
                                 o.data_ptr(), to.data_ptr(), lse.data_ptr(), ctypes.c_void_p(stream))
     _check(st, "attn_jvp_fwd")
     return o, to, lse
 
 
+def attn_fwd(q, k, v, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
+             out: Optional[Tuple] = None, stream=None):
+    """O, lse of masked attention (primal forward, bf16 inputs) on the GPU.
+
+    Same conventions as ``attn_jvp_fwd``; ``out`` may pass preallocated (o, lse).
+    """
+    import torch
+
+    ins = (q, k, v)
+    sh, (o,), lse, scale = _prepare(ins, out_dtype, scale, out, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd(ctypes.byref(sh), *(t.data_ptr() for t in ins), mask.handle, scale,
+                            o.data_ptr(), lse.data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_fwd")
+    return o, lse
+
+
 __all__ = [
     "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
-    "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_free", "attn_jvp_fwd", "LIB_PATH",
+    "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
+    "attn_jvp_fwd", "attn_fwd", "LIB_PATH",
 ]

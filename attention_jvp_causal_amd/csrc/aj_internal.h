@@ -13,8 +13,8 @@
 namespace aj {
 
 // Tile geometry of the kernels.  Every instantiation (bf16 / fp32, D = 64 / 128)
-// uses 128 query rows per workgroup (4 waves x 32 rows) and 64 keys per
-// streamed tile, so one key bitmask row is one 64-bit word.
+// uses 128 query rows per workgroup and 64 keys per streamed tile, so one key
+// bitmask row is one 64-bit word.
 constexpr int kTileM = 128;
 constexpr int kTileN = 64;
 constexpr int kMaxDevices = 64;
@@ -22,11 +22,25 @@ constexpr int kMaxDevices = 64;
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_dtype(int t) { return t == AJ_F32 || t == AJ_BF16; }
 
+// Which tangents a (query tile, key tile) pair carries, from the caller's
+// declaration of tokens whose tangents are zero (Entry::flags):
+//   kTileJvp       the general case: every product of the JVP
+//   kTileKeysFree  tK = tV = 0 on every key of the tile: tS = c tQ K^T and
+//                  (A + B) gets only (P.tS) V
+//   kTileAllFree   tQ = tK = tV = 0 for the whole tile: tS = 0, so only the
+//                  primal products remain
+// A query-tangent-free tile whose keys carry tangents runs as kTileJvp (tQ is
+// zero there and simply multiplies in).
+constexpr int32_t kTileJvp = 0;
+constexpr int32_t kTileKeysFree = 1;
+constexpr int32_t kTileAllFree = 3;
+
 // One run of key tiles visited by a query tile.  pidx < 0: every tile in
 // [kt0, kt1) is full.  pidx >= 0: the single tile kt0 (kt1 = kt0 + 1) is
-// partial and its per-row key bitmask starts at bits[pidx * kTileM].
+// partial and its per-row key bitmask starts at bits[pidx * kTileM].  Every
+// tile of a run has the same flags (one of the kTile* variants).
 struct Entry {
-  int32_t kt0, kt1, pidx, pad;
+  int32_t kt0, kt1, pidx, flags;
 };
 
 struct DeviceTables {
@@ -49,14 +63,18 @@ struct aj_mask_desc {
   std::vector<aj::Entry> entries;
   std::vector<int32_t> tasks;       // query tiles, most key tiles first
   std::vector<uint64_t> bits;       // partial_tiles * tile_m words
+  std::vector<int32_t> rects;       // the admissible rectangles {q0,q1,k0,k1}
+  std::vector<int32_t> tfree;       // merged tangent-free token ranges {t0,t1}
+  int64_t pairs_by_var[3] = {0, 0, 0};  // allowed pairs in kTileJvp / KeysFree / AllFree tiles
   std::mutex mu;                    // guards dev[]
   aj::DeviceTables dev[aj::kMaxDevices];
 };
 
 namespace aj {
-// Builds the tile map from validated, disjoint rectangles {q0,q1,k0,k1}.
+// Builds the tile map from validated, disjoint rectangles {q0,q1,k0,k1};
+// tfree holds n_tfree token ranges {t0,t1} whose tangents are declared zero.
 int32_t build_from_rects(int32_t seq_len, const int32_t* rects, int32_t n, int32_t head_dim,
-                         int32_t dtype, aj_mask_desc** out);
+                         int32_t dtype, const int32_t* tfree, int32_t n_tfree, aj_mask_desc** out);
 // Expands a frame-level layout into disjoint rectangles.
 int32_t layout_rects(const aj_mask_spec* spec, int32_t seq_len, std::vector<int32_t>* rects);
 }  // namespace aj

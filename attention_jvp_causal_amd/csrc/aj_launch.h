@@ -30,7 +30,11 @@ struct FwdArgs {
   const uint64_t* bits;
 };
 
-// Enqueues the forward kernel; returns an aj_status.
-int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, hipStream_t stream);
+// Enqueues the forward kernel; returns an aj_status.  jvp = false computes
+// only O and lse (tq, tk, tv and to are not used).  variants = true when the
+// descriptor declares tangent-free tiles: the kernel instance that skips
+// their zero products runs instead of the plain one.
+int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
+               hipStream_t stream);
 
 }  // namespace aj

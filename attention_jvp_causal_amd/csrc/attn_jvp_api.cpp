@@ -61,6 +61,73 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
   return AJ_OK;
 }
 
+// Checks the arguments shared by the forward entry points and fills the
+// common launch arguments (q, k, v, o, lse, strides, sizes, scale, tables).
+// ins = {q, k, v, ...}, outs = {o, [to,] lse}; every pointer non-null and
+// 16-byte aligned.
+int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void* const* outs, int n_out,
+                const aj_mask_desc* mask, float scale, aj::FwdArgs* a) {
+  if (!s || !mask) return AJ_EINVAL;
+  for (int i = 0; i < n_in; ++i)
+    if (!ins[i] || !aligned16(ins[i])) return AJ_EINVAL;
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i] || !aligned16(outs[i])) return AJ_EINVAL;
+  if (s->batch < 1 || s->heads < 1 || s->seq_len < 1) return AJ_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return AJ_EINVAL;
+  if (!aj::supported_head_dim(s->head_dim)) return AJ_ENOTSUP;
+  if (!aj::supported_dtype(s->in_dtype) || !aj::supported_dtype(s->out_dtype)) return AJ_ENOTSUP;
+  if (s->in_dtype == AJ_F32 && s->out_dtype != AJ_F32) return AJ_ENOTSUP;
+  const int64_t esz_in = s->in_dtype == AJ_F32 ? 4 : 2, esz_out = s->out_dtype == AJ_F32 ? 4 : 2;
+  const int64_t vin = 16 / esz_in, vout = 16 / esz_out;  // elements per 16 bytes
+  const int64_t D = s->head_dim, L = s->seq_len;
+  // strides: non-negative, 16-byte multiples, rows at least D apart
+  const int64_t is[3] = {s->in_stride_b, s->in_stride_h, s->in_stride_l};
+  const int64_t os[3] = {s->out_stride_b, s->out_stride_h, s->out_stride_l};
+  for (int i = 0; i < 3; ++i) {
+    if (is[i] < 0 || is[i] % vin != 0 || os[i] < 0 || os[i] % vout != 0) return AJ_EINVAL;
+  }
+  // input rows are read as whole rows through a 32-bit buffer range per key
+  // tile: distinct rows, and 64 rows' bytes must fit in 31 bits
+  if (is[2] < D || is[2] * esz_in * aj::kTileN >= (int64_t(1) << 31)) return AJ_EINVAL;
+  // outputs must not overlap themselves: sorted by stride, every stride must
+  // clear the extent of the axes below it (rows are D elements long).  Inputs
+  // are only read and may alias (a zero stride broadcasts).
+  {
+    int64_t st3[3][2] = {{os[0], s->batch}, {os[1], s->heads}, {os[2], L}};
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (st3[j][0] < st3[i][0]) std::swap(st3[i], st3[j]);
+    int64_t span = D;
+    for (int i = 0; i < 3; ++i) {
+      if (st3[i][1] == 1) continue;
+      if (st3[i][0] < span) return AJ_EINVAL;
+      span = st3[i][0] * st3[i][1];
+    }
+  }
+  if (mask->seq_len != s->seq_len || mask->head_dim != s->head_dim || mask->dtype != s->in_dtype)
+    return AJ_EMASK;
+  const int64_t BHL = int64_t(s->batch) * s->heads * L;
+  if (BHL > (int64_t(1) << 40)) return AJ_EINVAL;
+
+  const DeviceTables* t = nullptr;
+  int32_t st = device_tables(mask, &t);
+  if (st != AJ_OK) return st;
+
+  aj::FwdArgs& r = *a;
+  r = aj::FwdArgs{};
+  r.q = ins[0]; r.k = ins[1]; r.v = ins[2];
+  r.o = const_cast<void*>(outs[0]);
+  r.lse = static_cast<float*>(const_cast<void*>(outs[n_out - 1]));
+  r.isb = s->in_stride_b; r.ish = s->in_stride_h; r.isl = s->in_stride_l;
+  r.osb = s->out_stride_b; r.osh = s->out_stride_h; r.osl = s->out_stride_l;
+  r.B = s->batch; r.H = s->heads; r.L = s->seq_len;
+  r.n_tasks = mask->n_qt;
+  r.scale = scale;
+  r.scale_log2 = float(double(scale) * 1.4426950408889634074);
+  r.qt_off = t->qt_off; r.entries = t->entries; r.tasks = t->tasks; r.bits = t->bits;
+  return AJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,7 +156,8 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
     std::vector<int32_t> rects;
     const int32_t st = aj::layout_rects(spec, seq_len, &rects);
     if (st != AJ_OK) return st;
-    return aj::build_from_rects(seq_len, rects.data(), int32_t(rects.size() / 4), head_dim, dtype, out);
+    return aj::build_from_rects(seq_len, rects.data(), int32_t(rects.size() / 4), head_dim, dtype, nullptr, 0,
+                                out);
   } catch (const std::bad_alloc&) {
     return AJ_ENOMEM;
   } catch (...) {
@@ -99,7 +167,28 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
 
 int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
                                       int32_t head_dim, int32_t dtype, aj_mask_desc** out) {
-  return aj::build_from_rects(seq_len, rects, n_rects, head_dim, dtype, out);
+  return aj::build_from_rects(seq_len, rects, n_rects, head_dim, dtype, nullptr, 0, out);
+}
+
+int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t* ranges, int32_t n_ranges,
+                                        aj_mask_desc** out) {
+  if (!out) return AJ_EINVAL;
+  *out = nullptr;
+  if (!base) return AJ_EINVAL;
+  try {
+    return aj::build_from_rects(base->seq_len, base->rects.data(), int32_t(base->rects.size() / 4), base->head_dim,
+                                base->dtype, ranges, n_ranges, out);
+  } catch (const std::bad_alloc&) {
+    return AJ_ENOMEM;
+  } catch (...) {
+    return AJ_EINVAL;
+  }
+}
+
+int32_t attn_jvp_mask_desc_work(const aj_mask_desc* d, int64_t* pairs_by_variant) {
+  if (!d || !pairs_by_variant) return AJ_EINVAL;
+  for (int i = 0; i < 3; ++i) pairs_by_variant[i] = d->pairs_by_var[i];
+  return AJ_OK;
 }
 
 int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* d, aj_mask_stats* s) {
@@ -129,6 +218,13 @@ int32_t attn_jvp_mask_desc_tile_kind(const aj_mask_desc* d, int32_t qt, int32_t 
   return AJ_OK;
 }
 
+int32_t attn_jvp_mask_desc_tile_variant(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t* variant) {
+  if (!d || !variant || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt) return AJ_EINVAL;
+  const Entry* e = find_entry(d, qt, kt);
+  *variant = !e ? -1 : e->flags;
+  return AJ_OK;
+}
+
 int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t row,
                                     uint64_t* bits) {
   if (!d || !bits || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt || row < 0 || row >= d->tile_m)
@@ -155,62 +251,29 @@ void attn_jvp_mask_desc_free(aj_mask_desc* d) {
 int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq,
                      const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
                      void* to, float* lse, void* stream) {
-  if (!s || !mask) return AJ_EINVAL;
   const void* ins[6] = {q, k, v, tq, tk, tv};
   const void* outs[3] = {o, to, lse};
-  for (const void* p : ins)
-    if (!p || !aligned16(p)) return AJ_EINVAL;
-  for (const void* p : outs)
-    if (!p || !aligned16(p)) return AJ_EINVAL;
-  if (s->batch < 1 || s->heads < 1 || s->seq_len < 1) return AJ_EINVAL;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return AJ_EINVAL;
-  if (!aj::supported_head_dim(s->head_dim)) return AJ_ENOTSUP;
-  if (!aj::supported_dtype(s->in_dtype) || !aj::supported_dtype(s->out_dtype)) return AJ_ENOTSUP;
-  if (s->in_dtype == AJ_F32 && s->out_dtype != AJ_F32) return AJ_ENOTSUP;
-  const int64_t esz_in = s->in_dtype == AJ_F32 ? 4 : 2, esz_out = s->out_dtype == AJ_F32 ? 4 : 2;
-  const int64_t vin = 16 / esz_in, vout = 16 / esz_out;  // elements per 16 bytes
-  const int64_t D = s->head_dim, L = s->seq_len;
-  // strides: non-negative, 16-byte multiples, rows at least D apart
-  const int64_t is[3] = {s->in_stride_b, s->in_stride_h, s->in_stride_l};
-  const int64_t os[3] = {s->out_stride_b, s->out_stride_h, s->out_stride_l};
-  for (int i = 0; i < 3; ++i) {
-    if (is[i] < 0 || is[i] % vin != 0 || os[i] < 0 || os[i] % vout != 0) return AJ_EINVAL;
-  }
-  // outputs must not overlap themselves: sorted by stride, every stride must
-  // clear the extent of the axes below it (rows are D elements long).  Inputs
-  // are only read and may alias (a zero stride broadcasts).
-  {
-    int64_t st3[3][2] = {{os[0], s->batch}, {os[1], s->heads}, {os[2], L}};
-    for (int i = 0; i < 3; ++i)
-      for (int j = i + 1; j < 3; ++j)
-        if (st3[j][0] < st3[i][0]) std::swap(st3[i], st3[j]);
-    int64_t span = D;
-    for (int i = 0; i < 3; ++i) {
-      if (st3[i][1] == 1) continue;
-      if (st3[i][0] < span) return AJ_EINVAL;
-      span = st3[i][0] * st3[i][1];
-    }
-  }
-  if (mask->seq_len != s->seq_len || mask->head_dim != s->head_dim || mask->dtype != s->in_dtype)
-    return AJ_EMASK;
-  const int64_t BHL = int64_t(s->batch) * s->heads * L;
-  if (BHL > (int64_t(1) << 40)) return AJ_EINVAL;
-
-  const DeviceTables* t = nullptr;
-  int32_t st = device_tables(mask, &t);
-  if (st != AJ_OK) return st;
-
   aj::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv;
-  a.o = o; a.to = to; a.lse = lse;
-  a.isb = s->in_stride_b; a.ish = s->in_stride_h; a.isl = s->in_stride_l;
-  a.osb = s->out_stride_b; a.osh = s->out_stride_h; a.osl = s->out_stride_l;
-  a.B = s->batch; a.H = s->heads; a.L = s->seq_len;
-  a.n_tasks = mask->n_qt;
-  a.scale = scale;
-  a.scale_log2 = float(double(scale) * 1.4426950408889634074);
-  a.qt_off = t->qt_off; a.entries = t->entries; a.tasks = t->tasks; a.bits = t->bits;
-  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, static_cast<hipStream_t>(stream));
+  int32_t st = prepare(s, ins, 6, outs, 3, mask, scale, &a);
+  if (st != AJ_OK) return st;
+  a.tq = tq; a.tk = tk; a.tv = tv; a.to = to;
+  const bool variants = mask->pairs_by_var[1] + mask->pairs_by_var[2] > 0;
+  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, true, variants,
+                        static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
+                 float scale, void* o, float* lse, void* stream) {
+  const void* ins[3] = {q, k, v};
+  const void* outs[2] = {o, lse};
+  aj::FwdArgs a;
+  int32_t st = prepare(s, ins, 3, outs, 2, mask, scale, &a);
+  if (st != AJ_OK) return st;
+  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
+  a.tq = a.tk = a.tv = nullptr;
+  a.to = nullptr;
+  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, false, false,
+                        static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

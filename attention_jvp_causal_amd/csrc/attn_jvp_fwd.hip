@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "aj_internal.h"
 #include "aj_launch.h"
 
@@ -172,16 +174,18 @@ struct TileLoadPlan {
   }
 };
 
-// Issues the DMA of key tile [key0, key0 + BN) of the four tensors into one
-// LDS buffer.  Returns immediately; completion is tracked by vmcnt.  The
-// buffer resource ends at row L, so rows past the end read as zero.
-template <int NW, int D>
+// Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
+// when TANG, into one LDS buffer.  Returns immediately; completion is tracked
+// by vmcnt.  The buffer resource ends at row L, so rows past the end read as
+// zero.
+template <int NW, int D, bool TANG>
 __device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* const src[4], int64_t sl, int key0, int L,
                                                  int wave) {
-  const int nrec = int((int64_t)(L - key0) * sl * 2);
+  const int nrec = int((int64_t)min(L - key0, BN) * sl * 2);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
+    if (!TANG && (t & 1)) continue;  // tK, tV
     const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
 #pragma unroll
     for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
@@ -226,12 +230,13 @@ __device__ __forceinline__ float row4_sum(float x) {
 
 // ---- q16 shape --------------------------------------------------------------
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool JVP, bool VARIANTS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ16, 64 * kWavesQ16), amdgpu_waves_per_eu(2, 2)))
 void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   constexpr int NKS = D / 32;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 16;  // 16-row blocks of d for the value products
-  constexpr int NLOADS = TileLoadPlan<kWavesQ16, D>::PER_TILE;
+  constexpr int NL_ALL = TileLoadPlan<kWavesQ16, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
+  constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
   using Lds = Bf16Lds<D>;
   __shared__ __attribute__((aligned(1024))) Lds s;
 
@@ -243,9 +248,9 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
-  const uint16_t* __restrict__ tQg = (const uint16_t*)a.tq + in_off;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, (const uint16_t*)a.tk + in_off,
-                                  (const uint16_t*)a.v + in_off, (const uint16_t*)a.tv + in_off};
+  const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, JVP ? (const uint16_t*)a.tk + in_off : nullptr,
+                                  (const uint16_t*)a.v + in_off, JVP ? (const uint16_t*)a.tv + in_off : nullptr};
   const int q_row = qt * BM + wave * 16 + j16;
 
   // Q and tQ of this lane's query row, as B operands: k-step ks holds
@@ -257,7 +262,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks) {
       const int64_t off = q_row * a.isl + ks * 32 + 8 * g;
       Qr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
-      tQr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
+      tQr[ks] = as_bf16x8(JVP && q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
     }
   }
   // Q and tQ have landed before any DMA is in flight: the compiler tracks no
@@ -265,14 +270,33 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   wait_vmcnt<0>();
 
   const TileLoadPlan<kWavesQ16, D> plan(a.isl, wave, lane, swz_q16<D>);
+  // DMA of key tile kti of entry x (tangent tiles only where x carries them)
+  auto prefetch = [&](int b, const Entry& x, int kti) {
+    if (JVP && (!VARIANTS || x.flags == kTileJvp))
+      issue_tile_loads<kWavesQ16, D, true>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+    else
+      issue_tile_loads<kWavesQ16, D, false>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
+  };
+  // wait until at most the loads of x's tile (issued last) are in flight
+  auto wait_all_but = [&](const Entry& x) {
+    const bool bl = x.pidx >= 0 && wave == 0;
+    if (JVP && (!VARIANTS || x.flags == kTileJvp)) {
+      if (bl) wait_vmcnt<NL_ALL + 1>();
+      else wait_vmcnt<NL_ALL>();
+    } else {
+      if (bl) wait_vmcnt<NL_KV + 1>();
+      else wait_vmcnt<NL_KV>();
+    }
+  };
+
   const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
     en = a.entries[e];
     kt = en.kt0;
-    issue_tile_loads<kWavesQ16, D>(s.t[0], plan, src, a.isl, kt * BN, L, wave);
-    if (en.pidx >= 0 && wave == 0) issue_bits_load(s.bits[0], a.bits, en.pidx, lane);
+    prefetch(0, en, kt);
   }
 
   f32x4_t Oacc[NDB], ABacc[NDB];
@@ -307,36 +331,18 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     }
 
   int buf = 0;
-  while (e < e1) {
-    // next key tile into the other buffer while this one is computed
-    int e_n = e, kt_n = kt + 1;
-    Entry en_n = en;
-    if (kt_n >= en.kt1) {
-      e_n = e + 1;
-      if (e_n < e1) {
-        en_n = a.entries[e_n];
-        kt_n = en_n.kt0;
-      }
-    }
-    const bool has_next = e_n < e1;
-    if (has_next) {
-      issue_tile_loads<kWavesQ16, D>(s.t[buf ^ 1], plan, src, a.isl, kt_n * BN, L, wave);
-      if (en_n.pidx >= 0 && wave == 0) {
-        issue_bits_load(s.bits[buf ^ 1], a.bits, en_n.pidx, lane);
-        wait_vmcnt<NLOADS + 1>();
-      } else {
-        wait_vmcnt<NLOADS>();
-      }
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
+
+  // One 64-key tile of the variant VAR (which tangents the tile carries).
+  auto tile = [&](auto var_tag) __attribute__((always_inline)) {
+    constexpr int VAR = decltype(var_tag)::value;
+    constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
+    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
     const uint16_t* Kt = s.t[buf][0];
     const uint16_t* tKt = s.t[buf][1];
     const uint16_t* Vt = s.t[buf][2];
     const uint16_t* tVt = s.t[buf][3];
 
-    // ---- scores and score tangents of the 64-key tile (transposed) ----
+    // ---- scores and score tangents (transposed) ----
     // k-step outer, key block inner: four independent accumulator chains per
     // operand, so consecutive MFMAs never depend on each other.
     f32x4_t S[4], TS[4];
@@ -351,14 +357,20 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       for (int kb = 0; kb < 4; ++kb) {
         const int off = kb * 16 * D + koff[ks];
         kop[kb] = as_bf16x8(*(const u32x4_t*)(Kt + off));
-        tkop[kb] = as_bf16x8(*(const u32x4_t*)(tKt + off));
+        if constexpr (HAS_TKV) tkop[kb] = as_bf16x8(*(const u32x4_t*)(tKt + off));
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], Qr[ks], S[kb], 0, 0, 0);
+      if constexpr (HAS_TKV) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tkop[kb], Qr[ks], TS[kb], 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb)
+          TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tkop[kb], Qr[ks], TS[kb], 0, 0, 0);
+      }
+      if constexpr (HAS_TS) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], tQr[ks], TS[kb], 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb)
+          TS[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], tQr[ks], TS[kb], 0, 0, 0);
+      }
     }
     // lane holds keys 16kb + 4g + r of query row j16
 
@@ -371,7 +383,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
         for (int r = 0; r < 4; ++r) {
           const bool ok = (bits >> (16 * kb + r)) & 1ull;
           S[kb][r] = ok ? S[kb][r] : -INFINITY;
-          TS[kb][r] = ok ? TS[kb][r] : 0.f;
+          if constexpr (HAS_TS) TS[kb][r] = ok ? TS[kb][r] : 0.f;
         }
     }
 
@@ -388,14 +400,17 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
       m_run = need ? m_new : m_run;
       l_part *= alpha;
-      mu_part *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Oacc[db][r] *= alpha;
-          ABacc[db][r] *= alpha;
-        }
+        for (int r = 0; r < 4; ++r) Oacc[db][r] *= alpha;
+      if constexpr (JVP) {
+        mu_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ABacc[db][r] *= alpha;
+      }
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
@@ -410,17 +425,22 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
         f32x2_t p, u;
         p.x = fast_exp2(__builtin_fmaf(S[kb][r], sl2, -m_use));
         p.y = fast_exp2(__builtin_fmaf(S[kb][r + 1], sl2, -m_use));
-        u.x = p.x * (TS[kb][r] * c);
-        u.y = p.y * (TS[kb][r + 1] * c);
+        if constexpr (HAS_TS) {
+          u.x = p.x * (TS[kb][r] * c);
+          u.y = p.y * (TS[kb][r + 1] * c);
+        }
         const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
-        const bf16x2_t ub = __builtin_convertvector(u, bf16x2_t);
+        bf16x2_t ub;
+        if constexpr (HAS_TS) ub = __builtin_convertvector(u, bf16x2_t);
         l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
-        mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+        if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
         const int slot = 4 * (kb & 1) + r;
         P[kb >> 1][slot] = pb.x;
         P[kb >> 1][slot + 1] = pb.y;
-        U[kb >> 1][slot] = ub.x;
-        U[kb >> 1][slot + 1] = ub.y;
+        if constexpr (HAS_TS) {
+          U[kb >> 1][slot] = ub.x;
+          U[kb >> 1][slot + 1] = ub.y;
+        }
       }
 
     // ---- value products (transposed: rows = d, cols = queries) ----
@@ -438,18 +458,58 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
           const int off_b = 32 * p * D + voff[1][d4 + i];
           const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
           const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
-          const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
-          const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+          s16x4_t ta, tb;
+          if constexpr (HAS_TKV) {
+            ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
+            tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+          }
           vop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          tvop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+          if constexpr (HAS_TKV)
+            tvop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Oacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[i], P[p], Oacc[d4 + i], 0, 0, 0);
+        if constexpr (HAS_TS) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[i], U[p], ABacc[d4 + i], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[i], U[p], ABacc[d4 + i], 0, 0, 0);
+        }
+        if constexpr (HAS_TKV) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tvop[i], P[p], ABacc[d4 + i], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            ABacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tvop[i], P[p], ABacc[d4 + i], 0, 0, 0);
+        }
       }
+    }
+  };
+
+  while (e < e1) {
+    // next key tile into the other buffer while this one is computed
+    int e_n = e, kt_n = kt + 1;
+    Entry en_n = en;
+    if (kt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.entries[e_n];
+        kt_n = en_n.kt0;
+      }
+    }
+    if (e_n < e1) {
+      prefetch(buf ^ 1, en_n, kt_n);
+      wait_all_but(en_n);
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if constexpr (!JVP) {
+      tile(std::integral_constant<int, kTileAllFree>{});
+    } else if constexpr (!VARIANTS) {
+      tile(std::integral_constant<int, kTileJvp>{});
+    } else {
+      const int var = __builtin_amdgcn_readfirstlane(en.flags);
+      if (var == kTileJvp) tile(std::integral_constant<int, kTileJvp>{});
+      else if (var == kTileKeysFree) tile(std::integral_constant<int, kTileKeysFree>{});
+      else tile(std::integral_constant<int, kTileAllFree>{});
     }
     __syncthreads();  // every wave is done with this buffer before it is refilled
     e = e_n;
@@ -460,13 +520,15 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
 
   // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
   const float l_tot = row4_sum(l_part);
-  const float mu_tot = row4_sum(mu_part);
+  const float mu_tot = JVP ? row4_sum(mu_part) : 0.f;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // the lane's group, recomputed here rather than kept live across the loop
+  const int ge = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) >> 4;
   if (q_row < L) {
     const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d0 = db * 16 + 4 * g;
+      const int d0 = db * 16 + 4 * ge;
       f32x4_t ov, tv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -476,25 +538,26 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       }
       if constexpr (OUT_F32) {
         *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
-        *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+        if constexpr (JVP) *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
       } else {
         *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
-        *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
+        if constexpr (JVP) *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
       }
     }
-    if (g == 0)
+    if (ge == 0)
       a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 // ---- q32 shape --------------------------------------------------------------
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool JVP>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32), amdgpu_waves_per_eu(2, 2)))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
-  constexpr int NLOADS = TileLoadPlan<kWavesQ32, D>::PER_TILE;
+  constexpr int NL_ALL = TileLoadPlan<kWavesQ32, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
+  constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
   __shared__ __attribute__((aligned(1024))) Bf16Lds<D> s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -505,21 +568,43 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
-  const uint16_t* __restrict__ tQg = (const uint16_t*)a.tq + in_off;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, (const uint16_t*)a.tk + in_off,
-                                  (const uint16_t*)a.v + in_off, (const uint16_t*)a.tv + in_off};
+  const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, JVP ? (const uint16_t*)a.tk + in_off : nullptr,
+                                  (const uint16_t*)a.v + in_off, JVP ? (const uint16_t*)a.tv + in_off : nullptr};
   const int q_row = qt * BM + wave * 32 + l32;
 
-  // first key tile in flight before the prologue
   const TileLoadPlan<kWavesQ32, D> plan(a.isl, wave, lane, swz_q32<D>);
+  // At d = 64 the tangent-free variants are not built (three copies of the
+  // tile code do not fit the register budget of two workgroups per CU): every
+  // tile runs the general code, which is exact when the declared tangents are
+  // zero.
+  auto prefetch = [&](int b, const Entry& x, int kti) {
+    (void)x.flags;
+    if (JVP)
+      issue_tile_loads<kWavesQ32, D, true>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+    else
+      issue_tile_loads<kWavesQ32, D, false>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
+  };
+  auto wait_all_but = [&](const Entry& x) {
+    const bool bl = x.pidx >= 0 && wave == 0;
+    if (JVP) {
+      if (bl) wait_vmcnt<NL_ALL + 1>();
+      else wait_vmcnt<NL_ALL>();
+    } else {
+      if (bl) wait_vmcnt<NL_KV + 1>();
+      else wait_vmcnt<NL_KV>();
+    }
+  };
+
+  // first key tile in flight before the prologue
   const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
     en = a.entries[e];
     kt = en.kt0;
-    issue_tile_loads<kWavesQ32, D>(s.t[0], plan, src, a.isl, kt * BN, L, wave);
-    if (en.pidx >= 0 && wave == 0) issue_bits_load(s.bits[0], a.bits, en.pidx, lane);
+    prefetch(0, en, kt);
   }
 
   // Q and tQ of this lane's query row, as B operands: k-step kk holds
@@ -531,7 +616,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk) {
       const int64_t off = q_row * a.isl + kk * 16 + 8 * hi;
       Qr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
-      tQr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
+      tQr[kk] = as_bf16x8(JVP && q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
     }
   }
   // Q, tQ and the first key tile have landed; nothing the compiler tracks is
@@ -564,31 +649,12 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     }
 
   int buf = 0;
-  while (e < e1) {
-    // prefetch the next key tile into the other buffer
-    int e_n = e, kt_n = kt + 1;
-    Entry en_n = en;
-    if (kt_n >= en.kt1) {
-      e_n = e + 1;
-      if (e_n < e1) {
-        en_n = a.entries[e_n];
-        kt_n = en_n.kt0;
-      }
-    }
-    const bool has_next = e_n < e1;
-    if (has_next) {
-      issue_tile_loads<kWavesQ32, D>(s.t[buf ^ 1], plan, src, a.isl, kt_n * BN, L, wave);
-      // wait for all but the next tile's loads (issued last)
-      if (en_n.pidx >= 0 && wave == 0) {
-        issue_bits_load(s.bits[buf ^ 1], a.bits, en_n.pidx, lane);
-        wait_vmcnt<NLOADS + 1>();
-      } else {
-        wait_vmcnt<NLOADS>();
-      }
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
+
+  // One 64-key tile of the variant VAR (which tangents the tile carries).
+  auto tile = [&](auto var_tag) __attribute__((always_inline)) {
+    constexpr int VAR = decltype(var_tag)::value;
+    constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
+    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
     const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
     const uint16_t* Kt = s.t[buf][0];
     const uint16_t* tKt = s.t[buf][1];
@@ -605,10 +671,11 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = kb * 32 * D + koff[kk];
         const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
-        const bf16x8_t tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
+        bf16x8_t tkop;
+        if constexpr (HAS_TKV) tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
-        TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
-        TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, tQr[kk], TS, 0, 0, 0);
+        if constexpr (HAS_TKV) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
+        if constexpr (HAS_TS) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, tQr[kk], TS, 0, 0, 0);
       }
       // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
 
@@ -619,7 +686,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
           const bool ok = (bits >> key) & 1ull;
           S[r] = ok ? S[r] : -INFINITY;
-          TS[r] = ok ? TS[r] : 0.f;
+          if constexpr (HAS_TS) TS[r] = ok ? TS[r] : 0.f;
         }
       }
 
@@ -634,14 +701,17 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
         const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
         m_run = need ? m_new : m_run;
         l_part *= alpha;
-        mu_part *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            Oacc[db][r] *= alpha;
-            ABacc[db][r] *= alpha;
-          }
+          for (int r = 0; r < 16; ++r) Oacc[db][r] *= alpha;
+        if constexpr (JVP) {
+          mu_part *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ABacc[db][r] *= alpha;
+        }
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
@@ -656,16 +726,21 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
           f32x2_t p, u;
           p.x = fast_exp2(__builtin_fmaf(S[r], sl2, -m_use));
           p.y = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -m_use));
-          u.x = p.x * (TS[r] * c);
-          u.y = p.y * (TS[r + 1] * c);
+          if constexpr (HAS_TS) {
+            u.x = p.x * (TS[r] * c);
+            u.y = p.y * (TS[r + 1] * c);
+          }
           const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
-          const bf16x2_t ub = __builtin_convertvector(u, bf16x2_t);
+          bf16x2_t ub;
+          if constexpr (HAS_TS) ub = __builtin_convertvector(u, bf16x2_t);
           l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
-          mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+          if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
           P[st][t] = pb.x;
           P[st][t + 1] = pb.y;
-          U[st][t] = ub.x;
-          U[st][t + 1] = ub.y;
+          if constexpr (HAS_TS) {
+            U[st][t] = ub.x;
+            U[st][t + 1] = ub.y;
+          }
         }
 
       // ---- value products (transposed: rows = d, cols = queries) ----
@@ -679,16 +754,43 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
           const int off_b = (kb * 32 + 16 * st) * D + voff[1][db];
           const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
           const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
-          const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
-          const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+          s16x4_t ta, tb;
+          if constexpr (HAS_TKV) {
+            ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
+            tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+          }
           const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
           Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[st], Oacc[db], 0, 0, 0);
-          ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, U[st], ABacc[db], 0, 0, 0);
-          ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tvop, P[st], ABacc[db], 0, 0, 0);
+          if constexpr (HAS_TS) ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, U[st], ABacc[db], 0, 0, 0);
+          if constexpr (HAS_TKV) {
+            const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tvop, P[st], ABacc[db], 0, 0, 0);
+          }
         }
       }
     }
+  };
+
+  while (e < e1) {
+    // next key tile into the other buffer while this one is computed
+    int e_n = e, kt_n = kt + 1;
+    Entry en_n = en;
+    if (kt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.entries[e_n];
+        kt_n = en_n.kt0;
+      }
+    }
+    if (e_n < e1) {
+      prefetch(buf ^ 1, en_n, kt_n);
+      wait_all_but(en_n);
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{});
+    else tile(std::integral_constant<int, kTileJvp>{});
     __syncthreads();  // every wave is done with this buffer before it is refilled
     e = e_n;
     kt = kt_n;
@@ -698,7 +800,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
 
   // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
   const float l_tot = l_part + wave_xor32(l_part);
-  const float mu_tot = mu_part + wave_xor32(mu_part);
+  const float mu_tot = JVP ? mu_part + wave_xor32(mu_part) : 0.f;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_row < L) {
     const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
@@ -717,10 +819,10 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
         }
         if constexpr (OUT_F32) {
           *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
-          *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+          if constexpr (JVP) *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
         } else {
           *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
-          *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
+          if constexpr (JVP) *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
         }
       }
     if (hi == 0)
@@ -911,20 +1013,32 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 
-int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, hipStream_t stream) {
+template <bool JVP, bool VARIANTS>
+static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid, hipStream_t stream) {
+  const dim3 b16(64 * kWavesQ16), b32(64 * kWavesQ32);
+  if (head_dim == 128) {
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, JVP, VARIANTS>), grid, b16, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, JVP, VARIANTS>), grid, b16, 0, stream, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, JVP>), grid, b32, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, JVP>), grid, b32, 0, stream, a);
+  }
+}
+
+int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
+               hipStream_t stream) {
   const int64_t grid64 = int64_t(a.n_tasks) * a.B * a.H;
   if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
   const dim3 grid((unsigned)grid64);
-  const dim3 b16(64 * kWavesQ16), b32(64 * kWavesQ32), b_f32(NTHREADS);
   if (in_dtype == AJ_BF16) {
-    if (out_dtype == AJ_BF16) {
-      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false>), grid, b16, 0, stream, a);
-      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false>), grid, b32, 0, stream, a);
-    } else {
-      if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true>), grid, b16, 0, stream, a);
-      else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true>), grid, b32, 0, stream, a);
-    }
+    if (!jvp) launch_bf16<false, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);
+    else if (variants) launch_bf16<true, true>(a, out_dtype == AJ_F32, head_dim, grid, stream);
+    else launch_bf16<true, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);
   } else {
+    // fp32 inputs: the JVP only; tangent-free tiles run the general code
+    // (their tangents are zero, so every extra product adds zero)
+    if (!jvp) return AJ_ENOTSUP;
+    const dim3 b_f32(NTHREADS);
     if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<128>), grid, b_f32, 0, stream, a);
     else hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<64>), grid, b_f32, 0, stream, a);
   }

@@ -43,6 +43,44 @@ struct RectRef {
   int32_t q0, q1, k0, k1;
 };
 
+// Validates token ranges {t0, t1} (half-open, inside [0, L), may overlap) and
+// returns their sorted union.
+int32_t merge_ranges(int32_t L, const int32_t* t, int32_t n, std::vector<int32_t>* out) {
+  std::vector<std::pair<int32_t, int32_t>> v;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t a = t[2 * i], b = t[2 * i + 1];
+    if (a < 0 || a >= b || b > L) return AJ_EINVAL;
+    v.emplace_back(a, b);
+  }
+  std::sort(v.begin(), v.end());
+  out->clear();
+  for (const auto& x : v) {
+    if (!out->empty() && x.first <= out->back())
+      out->back() = std::max(out->back(), x.second);
+    else {
+      out->push_back(x.first);
+      out->push_back(x.second);
+    }
+  }
+  return AJ_OK;
+}
+
+// Whether [a, b) lies inside the union of the merged ranges r.
+bool covered(const std::vector<int32_t>& r, int32_t a, int32_t b) {
+  // last range starting at or before a
+  size_t lo = 0, hi = r.size() / 2;
+  while (lo < hi) {
+    const size_t mid = (lo + hi) / 2;
+    if (r[2 * mid] <= a) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo > 0 && r[2 * (lo - 1) + 1] >= b;
+}
+
+// Relative cost of one tile of each variant (units of 4d FLOP per pair).
+int64_t tile_cost(int32_t flags) { return flags == kTileJvp ? 3 : flags == kTileKeysFree ? 2 : 1; }
+int var_index(int32_t flags) { return flags == kTileJvp ? 0 : flags == kTileKeysFree ? 1 : 2; }
+
 }  // namespace
 
 int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out) {
@@ -80,12 +118,15 @@ int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out
 }
 
 int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,
-                         aj_mask_desc** out) {
+                         const int32_t* tf, int32_t n_tf, aj_mask_desc** out) {
   if (!out) return AJ_EINVAL;
   *out = nullptr;
-  if (L < 1 || n < 0 || (n > 0 && !r)) return AJ_EINVAL;
+  if (L < 1 || n < 0 || (n > 0 && !r) || n_tf < 0 || (n_tf > 0 && !tf)) return AJ_EINVAL;
   if (!supported_head_dim(head_dim) || !supported_dtype(dtype)) return AJ_ENOTSUP;
   int32_t st = validate_rects(L, r, n);
+  if (st != AJ_OK) return st;
+  std::vector<int32_t> tfree;
+  st = merge_ranges(L, tf, n_tf, &tfree);
   if (st != AJ_OK) return st;
 
   aj_mask_desc* d = new (std::nothrow) aj_mask_desc();
@@ -97,6 +138,15 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
     d->dtype = dtype;
     d->n_qt = (L + BM - 1) / BM;
     d->n_kt = (L + BN - 1) / BN;
+    d->rects.assign(r, r + 4 * size_t(n));
+    d->tfree = tfree;
+    // tangent-free query and key tiles: every token of the tile inside [0, L)
+    // is declared tangent-free
+    auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(L, qt * BM + BM)); };
+    auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(L, kt * BN + BN)); };
+    auto variant = [&](bool qf, int32_t kt) {
+      return k_free(kt) ? (qf ? kTileAllFree : kTileKeysFree) : kTileJvp;
+    };
 
     // bucket rectangles by the query tiles they touch
     std::vector<std::vector<RectRef>> per_qt(d->n_qt);
@@ -110,6 +160,7 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
     d->qt_off.assign(d->n_qt + 1, 0);
     for (int32_t qt = 0; qt < d->n_qt; ++qt) {
       d->qt_off[qt] = int32_t(d->entries.size());
+      const bool qf = q_free(qt);
       const int32_t a = qt * BM, b = std::min(L, a + BM);
       const int64_t full_count = int64_t(b - a) * BN;  // allowed pairs in a full tile
       // allowed-pair count per key tile: runs of interior tiles go into a
@@ -153,16 +204,21 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
         if (cnt == 0) continue;
         const bool in_range = int64_t(e1) * BN <= L;
         if (cnt == full_count && in_range) {
-          if (!d->entries.empty() && int32_t(d->entries.size()) > d->qt_off[qt] &&
-              d->entries.back().pidx < 0 && d->entries.back().kt1 == s0)
-            d->entries.back().kt1 = e1;  // extend the previous full run
-          else
-            d->entries.push_back(Entry{s0, e1, -1, 0});
+          for (int32_t kt = s0; kt < e1; ++kt) {
+            const int32_t fl = variant(qf, kt);
+            if (int32_t(d->entries.size()) > d->qt_off[qt] && d->entries.back().pidx < 0 &&
+                d->entries.back().kt1 == kt && d->entries.back().flags == fl)
+              d->entries.back().kt1 = kt + 1;  // extend the previous full run
+            else
+              d->entries.push_back(Entry{kt, kt + 1, -1, fl});
+            d->pairs_by_var[var_index(fl)] += full_count;
+          }
           d->full_tiles += e1 - s0;
         } else {
           for (int32_t kt = s0; kt < e1; ++kt) {
             const int32_t pidx = d->partial_tiles++;
-            d->entries.push_back(Entry{kt, kt + 1, pidx, 0});
+            const int32_t fl = variant(qf, kt);
+            d->entries.push_back(Entry{kt, kt + 1, pidx, fl});
             d->bits.resize(size_t(d->partial_tiles) * BM, 0);
             uint64_t* rowbits = &d->bits[size_t(pidx) * BM];
             const int32_t key0 = kt * BN;
@@ -173,16 +229,20 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
               const uint64_t m = (w == 64 ? ~0ull : ((1ull << w) - 1)) << (kk0 - key0);
               for (int32_t q = std::max(a, x.q0); q < std::min(b, x.q1); ++q) rowbits[q - a] |= m;
             }
+            int64_t c = 0;
+            for (int32_t row = 0; row < BM; ++row) c += __builtin_popcountll(rowbits[row]);
+            d->pairs_by_var[var_index(fl)] += c;
           }
         }
       }
       for (int32_t e = d->qt_off[qt]; e < int32_t(d->entries.size()); ++e)
-        work[qt] += d->entries[e].kt1 - d->entries[e].kt0;
+        work[qt] += (d->entries[e].kt1 - d->entries[e].kt0) * tile_cost(d->entries[e].flags);
     }
     d->qt_off[d->n_qt] = int32_t(d->entries.size());
 
     // tasks: every query tile (tiles with no allowed key still write zeros),
-    // most visited key tiles first; ties by larger tile index
+    // most work first (visited key tiles weighted by their variant's cost);
+    // ties by larger tile index
     d->tasks.resize(d->n_qt);
     for (int32_t qt = 0; qt < d->n_qt; ++qt) d->tasks[qt] = qt;
     std::stable_sort(d->tasks.begin(), d->tasks.end(), [&](int32_t x, int32_t y) {

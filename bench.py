@@ -8,6 +8,13 @@ Metric: TFLOP/s of unmasked work, counting 12*d FLOP per allowed
 (batch, head, query, key) pair (QK^T 2d, tQK^T + QtK^T 4d, P V 2d, P tV 2d,
 (P.tS) V 2d), as a fraction of the MI355X dense bf16 MFMA peak.
 
+Other measurements of the same kernels (one JSON line each, same schema):
+  --tangent-free   teacher-forcing workload with the clean half declared
+                   tangent-free: `value` stays in the 12d convention (the work
+                   of the plain JVP), the roofline counts the FLOPs executed
+                   (12d / 8d / 4d per pair by tile class);
+  --op fwd         primal masked attention (O, lse): 4d FLOP per pair.
+
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -28,6 +35,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak, 1 GPU"
+METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", "attn_jvp_fwd.hip")
 
 
@@ -43,12 +51,14 @@ def kernel_sha() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def kernel_name(dtype: str, head_dim: int, out_f32: bool) -> str:
+def kernel_name(dtype: str, head_dim: int, out_f32: bool, jvp: bool = True, variants: bool = False) -> str:
     """Name of the kernel instance the library launches for this configuration."""
     if dtype == "f32":
         return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
-    kind = "q16" if head_dim == 128 else "q32"
-    return f"attn_jvp_fwd_bf16_{kind}_kernel<{head_dim}, {'true' if out_f32 else 'false'}>"
+    b = lambda x: "true" if x else "false"
+    if head_dim == 128:
+        return f"attn_jvp_fwd_bf16_q16_kernel<128, {b(out_f32)}, {b(jvp)}, {b(jvp and variants)}>"
+    return f"attn_jvp_fwd_bf16_q32_kernel<64, {b(out_f32)}, {b(jvp)}>"
 
 
 def measured_traffic(workload: str):
@@ -154,6 +164,10 @@ def main(argv=None):
     ap.add_argument("--workload", default=None, help="workload name (default: the c3-3 Wan2.1-1.3B shape)")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads timed for the oracle baseline (0 = skip)")
+    ap.add_argument("--op", default="jvp", choices=["jvp", "fwd"],
+                    help="jvp: O, tO, lse (the metric); fwd: primal O, lse only")
+    ap.add_argument("--tangent-free", action="store_true",
+                    help="declare the clean half of a teacher-forcing workload tangent-free")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -185,8 +199,19 @@ def main(argv=None):
     dev = {n: t.to("cuda:0") for n, t in inputs.items()}
     desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
                                        head_dim=w.head_dim, dtype=w.dtype)
+    if args.tangent_free:
+        if not w.clean_tangent_zero:
+            raise SystemExit(f"--tangent-free needs a workload whose clean half has zero tangents, not {w.name}")
+        desc = aj.attn_jvp_mask_desc_tangent_free(desc, [(0, w.seq_len // 2)])
     pairs = desc.unmasked_pairs * w.batch * w.heads
-    flop = 12.0 * w.head_dim * pairs
+    per_pair = 12.0 if args.op == "jvp" else 4.0
+    flop = per_pair * w.head_dim * pairs
+    # FLOPs the kernel executes: fewer than the convention's on tangent-free tiles
+    if args.op == "jvp":
+        wk = desc.work()
+        exec_flop = float(w.head_dim) * w.batch * w.heads * (12.0 * wk[0] + 8.0 * wk[1] + 4.0 * wk[2])
+    else:
+        exec_flop = flop
     out_dtype = {None: None, "bf16": torch.bfloat16, "f32": torch.float32}[args.out_dtype]
     B, H, L, D = w.shape
     odt = out_dtype or dev["q"].dtype
@@ -196,7 +221,10 @@ def main(argv=None):
     args_ = [dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")]
 
     def step():
-        aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
+        if args.op == "jvp":
+            aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
+        else:
+            aj.attn_fwd(*args_[:3], desc, scale=w.scale, out_dtype=out_dtype, out=(outs[0], outs[2]))
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -225,18 +253,22 @@ def main(argv=None):
     ms_per_step = wall * 1e3 / args.steps
 
     value = flop / (ms_per_step * 1e-3) / 1e12
-    achieved = flop / (avg_ms * 1e-3) / 1e12
+    achieved = exec_flop / (avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     traffic = measured_traffic(w.name)
-    in_bytes = 6 * B * H * L * D * inputs["q"].element_size()
-    out_bytes = 2 * B * H * L * D * odt.itemsize + B * H * L * 4
+    n_in, n_out = (6, 2) if args.op == "jvp" else (3, 1)
+    in_bytes = n_in * B * H * L * D * inputs["q"].element_size()
+    out_bytes = n_out * B * H * L * D * odt.itemsize + B * H * L * 4
+    if args.op != "jvp" or args.tangent_free:
+        traffic = None  # counters are recorded for the plain JVP only
 
     cpu = None
-    if args.cpu_heads > 0:
+    if args.cpu_heads > 0 and args.op == "jvp":
         cpu = cpu_baseline(w, inputs, min(args.cpu_heads, w.heads))
 
+    metric = METRIC if args.op == "jvp" else METRIC_FWD
     rec = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -255,6 +287,11 @@ def main(argv=None):
                     f"frames_per_chunk={w.frames_per_chunk}",
             "unmasked_pairs": pairs,
             "flop_per_step": flop,
+            "op": args.op,
+            "tangent_free": ("clean half [0, L/2) declared tangent-free; value counts 12d per pair, "
+                             "roofline the executed 12d / 8d / 4d per pair by tile class")
+                            if args.tangent_free else None,
+            "executed_flop_per_step": exec_flop,
             "out_dtype": str(odt).replace("torch.", ""),
             "parallelism": "single GPU",
         },
@@ -266,7 +303,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": kernel_name(w.dtype, D, odt == torch.float32),
+            "kernel": kernel_name(w.dtype, D, odt == torch.float32, args.op == "jvp", args.tangent_free),
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,

@@ -117,6 +117,33 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
 int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
                                       int32_t head_dim, int32_t dtype, aj_mask_desc** out);
 
+/* Derive a descriptor that also knows which tokens carry no tangent.
+ * In teacher-forcing sCM / MeanFlow the JVP runs through the packed
+ * [clean | noisy] forward and the clean context has zero tangent (Sec. 3.1.2);
+ * then most of the JVP's products vanish: for a query whose tangent is zero,
+ * attending keys whose tangents are zero, only the primal products remain;
+ * for a key whose tangents are zero, tS reduces to scale * <tq, k> and the tV
+ * product drops.
+ * ranges holds n_ranges half-open token intervals {t0, t1} inside
+ * [0, seq_len) (they may overlap); the new descriptor has base's mask, head_dim
+ * and dtype.  By passing it to attn_jvp_fwd the caller declares that tq, tk
+ * and tv are exactly zero at these tokens (for every batch and head); the
+ * kernel then skips the products that are zero, per tile of 128 queries x 64
+ * keys that lies entirely inside the ranges, and need not read those
+ * tangents.  The result equals attn_jvp_fwd with the plain descriptor
+ * whenever the declaration holds; if it does not, the tangent output is
+ * unspecified.  Host-only.  Errors: AJ_EINVAL (null pointers, bad range),
+ * AJ_ENOMEM.  On error *out is set to NULL. */
+int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t* ranges, int32_t n_ranges,
+                                        aj_mask_desc** out);
+
+/* Allowed (query, key) pairs per (batch, head) by the work the kernel does on
+ * them: pairs_by_variant[0] in tiles with all JVP products (12 D FLOP per
+ * pair), [1] in tiles whose keys carry no tangent (8 D), [2] in tiles where
+ * neither queries nor keys do (4 D, the primal products only).  Without
+ * tangent-free ranges every pair is in [0].  Errors: AJ_EINVAL on null. */
+int32_t attn_jvp_mask_desc_work(const aj_mask_desc* desc, int64_t* pairs_by_variant);
+
 /* Summary of a descriptor.  Errors: AJ_EINVAL on null arguments. */
 int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* desc, aj_mask_stats* out);
 
@@ -124,6 +151,13 @@ int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* desc, aj_mask_stats* out);
  * Errors: AJ_EINVAL on null arguments or out-of-range tile indices. */
 int32_t attn_jvp_mask_desc_tile_kind(const aj_mask_desc* desc, int32_t q_tile, int32_t k_tile,
                                      int32_t* kind);
+
+/* Work variant of tile (q_tile, k_tile): -1 skipped, 0 all JVP products,
+ * 1 keys carry no tangent, 3 neither queries nor keys carry tangents (see
+ * attn_jvp_mask_desc_tangent_free).  Errors: AJ_EINVAL on null arguments or
+ * out-of-range tile indices. */
+int32_t attn_jvp_mask_desc_tile_variant(const aj_mask_desc* desc, int32_t q_tile, int32_t k_tile,
+                                        int32_t* variant);
 
 /* Key bitmask of one query row of a tile: bit j set when key
  * k_tile * tile_n + j is allowed for query q_tile * tile_m + row.  For full
@@ -154,7 +188,8 @@ typedef struct {
 /* Forward-mode JVP of masked attention: writes O, tO ([B, H, L, D], out_dtype)
  * and lse ([B, H, L] float32) for inputs q, k, v, tq, tk, tv ([B, H, L, D],
  * in_dtype), all device pointers, 16-byte aligned, strides multiples of
- * 16 bytes / element size.  scale multiplies the scores and their tangents;
+ * 16 bytes / element size, in_stride_l >= D and 64 * in_stride_l * element
+ * size < 2^31.  scale multiplies the scores and their tangents;
  * pass 1/sqrt(D) for the usual softmax scale.  Rows with no allowed key get
  * O = tO = 0 and lse = -inf.  Input values at masked-out positions must be
  * finite (they are read for partial tiles and multiplied by zero).
@@ -168,6 +203,16 @@ typedef struct {
 int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const void* v,
                      const void* tq, const void* tk, const void* tv, const aj_mask_desc* mask,
                      float scale, void* o, void* to, float* lse, void* stream);
+
+/* Primal masked attention (Eq. 42): O = softmax(scale * Q K^T + M) V and lse,
+ * the forward of the student's packed teacher-forcing attention (Sec. 3.1.1,
+ * Eq. 8) on the same descriptor as the JVP.  Same shapes, strides, checks and
+ * results for O and lse as attn_jvp_fwd (bit for bit: the same kernel code
+ * without the tangent products); in_dtype must be AJ_BF16 (AJ_ENOTSUP
+ * otherwise).  o is [B, H, L, D] out_dtype, lse [B, H, L] float32.
+ * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
+int32_t attn_fwd(const aj_shape* shape, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
+                 float scale, void* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }
