@@ -19,12 +19,16 @@ PyTorch's scaled_dot_product_attention and scipy's logsumexp as library special
 cases, per-element brute force on tiny inputs, the invariants of the JVP
 (linearity, zero tangents, tQ = tK = 0, masked-key perturbation, constant
 values, shift invariance), closed-form pair counts and hand-written frame-level
-mask grids.  Every function here is pinned; none is "parity unpinned".
+mask grids.  The gradients (tests/test_oracle_vjp.py) are pinned by reverse-mode
+autodiff of a dense masked attention and of PyTorch's SDPA, by the adjoint
+identity with the (separately pinned) JVP, by central finite differences and by
+their sum rules.  Every function here is pinned; none is "parity unpinned".
 """
 from .masks import MaskLayout, RectMask, allowed, key_ranges, dense_mask, unmasked_pairs
 from .attention_jvp import attn_jvp_ref, unmasked_pairs_rows
+from .attention_vjp import attn_vjp_ref, attn_vjp_sampled
 
 __all__ = [
     "MaskLayout", "RectMask", "allowed", "key_ranges", "dense_mask", "unmasked_pairs",
-    "attn_jvp_ref", "unmasked_pairs_rows",
+    "attn_jvp_ref", "unmasked_pairs_rows", "attn_vjp_ref", "attn_vjp_sampled",
 ]
