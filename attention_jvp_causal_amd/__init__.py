@@ -79,10 +79,12 @@ def lib() -> ctypes.CDLL:
     L.attn_jvp_mask_desc_tile_variant.argtypes = [pdesc, i32, i32, ctypes.POINTER(i32)]
     L.attn_jvp_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
     L.attn_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, pdesc, f32, P, P, P]
+    L.attn_bwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P, P]
+    L.attn_jvp_mask_desc_col_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
                "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
                "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
-               "attn_fwd"):
+               "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -155,6 +157,13 @@ class MaskDesc:
         b = ctypes.c_uint64()
         _check(lib().attn_jvp_mask_desc_row_bits(self.handle, q_tile, k_tile, row, ctypes.byref(b)),
                "attn_jvp_mask_desc_row_bits")
+        return b.value
+
+    def col_bits(self, k_tile: int, q_tile: int, key_row: int) -> int:
+        """Bitmask over the 64 queries of q_tile that may attend key k_tile*128 + key_row."""
+        b = ctypes.c_uint64()
+        _check(lib().attn_jvp_mask_desc_col_bits(self.handle, k_tile, q_tile, key_row, ctypes.byref(b)),
+               "attn_jvp_mask_desc_col_bits")
         return b.value
 
     def close(self) -> None:
@@ -294,9 +303,38 @@ def attn_fwd(q, k, v, mask: MaskDesc, scale: Optional[float] = None, out_dtype=N
     return o, lse
 
 
+def attn_bwd(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
+             out: Optional[Tuple] = None, stream=None):
+    """dq, dk, dv of masked attention for the cotangent ``dout`` (bf16 inputs).
+
+    ``o`` and ``lse`` are the forward's outputs for the same inputs, mask and
+    scale.  Returns (dq, dk, dv, delta): the gradients [B, H, L, D] in
+    ``out_dtype`` (default bf16) and delta = rowsum(dout * o) [B, H, L] float32.
+    ``out`` may pass preallocated (dq, dk, dv, delta).
+    """
+    import torch
+
+    ins = (q, k, v, o, dout)
+    x0 = q
+    B, H, L, D = x0.shape
+    if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != x0.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on the inputs' device")
+    if out is None:
+        sh, (dq, dk, dv), delta, scale = _prepare(ins, out_dtype, scale, None, 3)
+    else:
+        sh, (dq, dk, dv), delta, scale = _prepare(ins, out_dtype, scale, tuple(out), 3)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd(ctypes.byref(sh), *(t.data_ptr() for t in ins), lse.data_ptr(), mask.handle, scale,
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_bwd")
+    return dq, dk, dv, delta
+
+
 __all__ = [
     "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
     "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
-    "attn_jvp_fwd", "attn_fwd", "LIB_PATH",
+    "attn_jvp_fwd", "attn_fwd", "attn_bwd", "LIB_PATH",
 ]

@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the gfx950 kernels of this library:
+// vector types, the direct buffer -> LDS DMA of 16-byte chunks into swizzled
+// tiles, explicit vmcnt waits, and the cross-lane reductions over the lanes
+// that share one row of an MFMA accumulator.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aj_internal.h"
+
+namespace aj {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BM = kTileM;   // query rows per workgroup
+constexpr int BN = kTileN;   // keys per streamed tile
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+template <int D>
+__device__ __forceinline__ int swz_q16(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_q32(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer resource: 32-bit data, no swizzle
+
+// One direct buffer -> LDS load of 16 bytes per lane: lane l's chunk lands at
+// LDS byte address lds_base + 16 l.  Written as inline asm so that the
+// compiler does not track it: the kernel waits for these loads itself
+// (wait_vmcnt) right before the barrier that publishes a buffer, instead of
+// the compiler's conservative wait for every load in flight into any buffer.
+// The instruction has no register results; it only writes LDS.  m0 is set
+// here and used by nothing else in these kernels (checked by a build test).
+__device__ __forceinline__ void lds_dma_16(uint32_t lds_base, uint32_t voffset, i32x4_t rsrc) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4_t rs;
+  rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  rs.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);  // stride 0
+  rs.z = __builtin_amdgcn_readfirstlane(nbytes);
+  rs.w = kRsrcWord3;
+  return rs;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// Per-lane byte offsets (inside one key tile of one tensor) of the 16-byte
+// chunks this lane moves.  Wave instruction i fills 1 KB block blk = wave +
+// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. row r = chunk /
+// CH at swizzled position p, so it fetches logical chunk p ^ swz(r) of row r.
+template <int NW, int D>
+struct TileLoadPlan {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int NI = (BN * CH) / (64 * NW);   // wave instructions per tensor
+  static constexpr int PER_TILE = 4 * NI;            // DMA instructions per wave per tile
+  uint32_t voff[NI];
+  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ci = (wave + NW * i) * 64 + lane;
+      const int r = ci / CH, p = ci % CH;
+      voff[i] = uint32_t(r * sl * 2 + ((p ^ swz(r)) << 4));
+    }
+  }
+};
+
+// Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx.
+__device__ __forceinline__ void issue_bits_load(uint64_t* dst, const uint64_t* bits, int pidx, int lane) {
+  lds_dma_16(lds_addr(dst), uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// max over lanes l and l^32 (the two halves of one q32 query row) without
+// the LDS pipe: v_permlane32_swap exchanges the upper half of one operand with
+// the lower half of the other.
+__device__ __forceinline__ float row_max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 of one q16 query row
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+}  // namespace aj

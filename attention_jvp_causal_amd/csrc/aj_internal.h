@@ -43,12 +43,32 @@ struct Entry {
   int32_t kt0, kt1, pidx, flags;
 };
 
-struct DeviceTables {
-  void* base = nullptr;         // one hipMalloc holding everything below
+// A tile map over one orientation of the mask: for every tile of kTileM
+// rows (the "owner" axis) the runs of kTileN-wide tiles of the other axis it
+// must visit, per-row bitmasks of its partial tiles and a longest-first task
+// order.  The row map (owner = query tiles) drives the forward kernels and the
+// dQ kernel; the column map (owner = key tiles, built from the transposed
+// rectangles) drives the dK / dV kernel.
+struct TileMap {
+  int32_t n_qt = 0, n_kt = 0;       // owner tiles, visited-axis tiles
+  int32_t full_tiles = 0, partial_tiles = 0;
+  int64_t pairs_by_var[3] = {0, 0, 0};  // allowed pairs in kTileJvp / KeysFree / AllFree tiles
+  std::vector<int32_t> qt_off;      // n_qt + 1 offsets into entries
+  std::vector<Entry> entries;
+  std::vector<int32_t> tasks;       // owner tiles, most work first
+  std::vector<uint64_t> bits;       // partial_tiles * kTileM words
+};
+
+struct DeviceMap {
   const int32_t* qt_off = nullptr;
   const Entry* entries = nullptr;
   const int32_t* tasks = nullptr;
   const uint64_t* bits = nullptr;
+};
+
+struct DeviceTables {
+  void* base = nullptr;  // one hipMalloc holding both maps
+  DeviceMap rows, cols;
 };
 
 }  // namespace aj
@@ -56,16 +76,11 @@ struct DeviceTables {
 struct aj_mask_desc {
   int32_t seq_len = 0, head_dim = 0, dtype = 0;
   int32_t tile_m = aj::kTileM, tile_n = aj::kTileN;
-  int32_t n_qt = 0, n_kt = 0;
   int64_t pairs = 0;
-  int32_t full_tiles = 0, partial_tiles = 0;
-  std::vector<int32_t> qt_off;      // n_qt + 1 offsets into entries
-  std::vector<aj::Entry> entries;
-  std::vector<int32_t> tasks;       // query tiles, most key tiles first
-  std::vector<uint64_t> bits;       // partial_tiles * tile_m words
   std::vector<int32_t> rects;       // the admissible rectangles {q0,q1,k0,k1}
   std::vector<int32_t> tfree;       // merged tangent-free token ranges {t0,t1}
-  int64_t pairs_by_var[3] = {0, 0, 0};  // allowed pairs in kTileJvp / KeysFree / AllFree tiles
+  aj::TileMap rows;                 // query tiles -> key-tile runs
+  aj::TileMap cols;                 // key tiles -> query-tile runs (transposed mask)
   std::mutex mu;                    // guards dev[]
   aj::DeviceTables dev[aj::kMaxDevices];
 };

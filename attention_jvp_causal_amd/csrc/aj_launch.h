@@ -30,6 +30,32 @@ struct FwdArgs {
   const uint64_t* bits;
 };
 
+// Arguments of the gradient kernels (bf16 inputs [B, H, L, D] sharing the
+// input strides; dq, dk, dv sharing the output strides; lse and delta
+// contiguous [B, H, L] float32).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;  // written by the dQ kernel, read by the dK / dV kernel
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t isb, ish, isl;
+  int64_t osb, osh, osl;
+  int32_t B, H, L, n_row_tasks, n_col_tasks;
+  float scale;
+  float scale_log2;
+  DeviceMap rows;  // query tiles -> key-tile runs
+  DeviceMap cols;  // key tiles -> query-tile runs
+};
+
+// Enqueues the dQ kernel and then the dK / dV kernel on `stream`.
+int launch_bwd(const BwdArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+
 // Enqueues the forward kernel; returns an aj_status.  jvp = false computes
 // only O and lse (tq, tk, tv and to are not used).  variants = true when the
 // descriptor declares tangent-free tiles: the kernel instance that skips

@@ -1,0 +1,511 @@
+// Gradients of masked attention for gfx950 (MI355X): dQ, dK and dV for a
+// cotangent dO, on the mask descriptor of the forward pass.
+//
+// Training through the packed teacher-forcing forward ("Causal-rCM",
+// Sec. 3.1.1, Eq. 8) differentiates one masked attention (Eq. 42).  With the
+// forward's lse, P_ij = exp(c <q_i, k_j> - lse_i) on allowed pairs, and
+//   D_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - D_i),
+//   dQ_i = c sum_j dS_ij k_j,  dK_j = c sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+//
+// Two kernels, no atomics (results are deterministic):
+// * dQ (query-parallel, the forward's tile map): a workgroup owns a 128-row
+//   query tile and streams its admissible 64-key tiles of K and V.  As in the
+//   forward, the scores are computed transposed (S^T = K Q^T, dP^T = V dO^T
+//   with Q and dO of the lane's row held as MFMA B operands), so the row
+//   statistics lse and D are one value per lane and the dS accumulator feeds
+//   dQ^T += K^T dS^T directly, K^T coming from LDS transpose reads.  It also
+//   computes and stores D.
+// * dK / dV (key-parallel, the transposed tile map): a workgroup owns a tile
+//   of 128 keys and streams the admissible 64-query tiles of Q and dO (plus
+//   their lse and D).  Here the scores are computed untransposed (S = Q K^T,
+//   dP = dO V^T with K and V of the lane's key as B operands): one key per
+//   lane column, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly,
+//   dO^T and Q^T coming from transpose reads.
+// Both use 8 waves of 16 rows (v_mfma_f32_16x16x32_bf16, two waves per
+// SIMD), the direct buffer -> LDS DMA into a double buffer and the swizzled
+// tile layout of the forward kernels.  Masked pairs are removed by select
+// (P = dS = 0), never by arithmetic on -inf.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aj_device.h"
+#include "aj_internal.h"
+#include "aj_launch.h"
+
+namespace aj {
+
+constexpr int kBwdWaves = 8;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct BwdLds {
+  static constexpr int TILE = BN * D;  // elements per tensor tile
+  uint16_t t[2][2][TILE];              // [buffer][(K, V) for dQ | (Q, dO) for dK, dV]
+  uint64_t bits[2][BM];                // per-row bitmask of a partial tile
+  float rowv[2][2][256];               // [buffer][lse, D] of the 64 streamed queries
+};
+
+// One direct buffer -> LDS load of 4 bytes per lane (lane l's dword lands at
+// lds_base + 4 l); out-of-range dwords read as zero.  Same rules as lds_dma_16.
+__device__ __forceinline__ void lds_dma_4(uint32_t lds_base, uint32_t voffset, i32x4_t rsrc) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// DMA of rows [row0, row0 + BN) of two [L, D] tensors into one LDS buffer.
+template <int D>
+__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<kBwdWaves, D>& plan,
+                                                 const uint16_t* s0, const uint16_t* s1, int64_t sl, int row0, int L,
+                                                 int wave) {
+  const int nrec = int((int64_t)min(L - row0, BN) * sl * 2);
+  const i32x4_t r0 = make_rsrc(s0 + (int64_t)row0 * sl, nrec);
+  const i32x4_t r1 = make_rsrc(s1 + (int64_t)row0 * sl, nrec);
+#pragma unroll
+  for (int i = 0; i < TileLoadPlan<kBwdWaves, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[0] + (wave + kBwdWaves * i) * 512), plan.voff[i], r0);
+#pragma unroll
+  for (int i = 0; i < TileLoadPlan<kBwdWaves, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[1] + (wave + kBwdWaves * i) * 512), plan.voff[i], r1);
+}
+
+__device__ __forceinline__ float bf16_dot8(bf16x8_t x, bf16x8_t y, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2_t a = {x[e], x[e + 1]}, b = {y[e], y[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+  }
+  return acc;
+}
+
+// ---- dQ (and D) ---------------------------------------------------------------
+
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NKS = D / 32;  // MFMA k-steps over d for S^T and dP^T
+  constexpr int NDB = D / 16;  // 16-row blocks of d for dQ^T
+  constexpr int NL = 2 * TileLoadPlan<kBwdWaves, D>::NI;  // DMA per wave per tile
+  __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int qt = a.rows.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t bhL = (int64_t)bh * L;
+  const uint16_t* Kg = (const uint16_t*)a.k + in_off;
+  const uint16_t* Vg = (const uint16_t*)a.v + in_off;
+  const int q_row = qt * BM + wave * 16 + j16;
+
+  // Q, dO of this lane's row as B operands (k-step ks: d = 32ks + 8g ..),
+  // D = <dO, O> and the row's lse
+  bf16x8_t Qr[NKS], dOr[NKS];
+  float dpart = 0.f;
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const uint16_t* Qg = (const uint16_t*)a.q + in_off;
+    const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
+    const uint16_t* Og = (const uint16_t*)a.o + in_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int64_t off = q_row * a.isl + ks * 32 + 8 * g;
+      Qr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
+      dOr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(dOg + off) : zero);
+      const bf16x8_t Or = as_bf16x8(q_row < L ? *(const u32x4_t*)(Og + off) : zero);
+      dpart = bf16_dot8(dOr[ks], Or, dpart);
+    }
+  }
+  const float lse_l2 = q_row < L ? a.lse[bhL + q_row] * kLog2e : 0.f;
+  wait_vmcnt<0>();
+  const float delta = row4_sum(dpart);
+
+  const TileLoadPlan<kBwdWaves, D> plan(a.isl, wave, lane, swz_q16<D>);
+  auto prefetch = [&](int b, const Entry& x, int kti) {
+    issue_pair_loads<D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.rows.bits, x.pidx, lane);
+  };
+  const int e0 = a.rows.qt_off[qt], e1 = a.rows.qt_off[qt + 1];
+  int e = e0, kt = 0;
+  Entry en = {0, 0, -1, 0};
+  if (e < e1) {
+    en = a.rows.entries[e];
+    kt = en.kt0;
+    prefetch(0, en, kt);
+  }
+
+  f32x4_t dQacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dQacc[db][r] = 0.f;
+  const float sl2 = a.scale_log2;
+
+  // LDS offsets as in the forward kernel: row operand of 16-key block kb,
+  // k-step ks at kb*16*D + koff[ks]; transpose-read operand of value k-step p,
+  // d block db at 32p*D + voff[h][db].
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
+  const int vrow = 4 * g + (j16 >> 2);
+  int voff[2][NDB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow + 16 * h;
+      const int chunk = 2 * db + ((j16 & 3) >> 1);
+      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
+    }
+
+  int buf = 0;
+  while (e < e1) {
+    int e_n = e, kt_n = kt + 1;
+    Entry en_n = en;
+    if (kt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.rows.entries[e_n];
+        kt_n = en_n.kt0;
+      }
+    }
+    if (e_n < e1) {
+      prefetch(buf ^ 1, en_n, kt_n);
+      if (en_n.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
+      else wait_vmcnt<NL>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const uint16_t* Kt = s.t[buf][0];
+    const uint16_t* Vt = s.t[buf][1];
+
+    // S^T = K Q^T and dP^T = V dO^T for the 64 keys of the tile
+    f32x4_t S[4], dP[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[kb][r] = dP[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8_t kop[4], vop[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int off = kb * 16 * D + koff[ks];
+        kop[kb] = as_bf16x8(*(const u32x4_t*)(Kt + off));
+        vop[kb] = as_bf16x8(*(const u32x4_t*)(Vt + off));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], Qr[ks], S[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        dP[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[kb], dOr[ks], dP[kb], 0, 0, 0);
+    }
+    // lane holds keys 16kb + 4g + r of query row j16
+
+    uint64_t bits = ~0ull;
+    if (en.pidx >= 0) bits = s.bits[buf][wave * 16 + j16] >> (4 * g);
+    // dS = P (dP - D), rounded to bf16 once; value k-step p takes key blocks
+    // 2p (slots 0..3) and 2p+1 (slots 4..7)
+    bf16x8_t DS[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const bool ok0 = (bits >> (16 * kb + r)) & 1ull, ok1 = (bits >> (16 * kb + r + 1)) & 1ull;
+        f32x2_t ds;
+        const float p0 = fast_exp2(__builtin_fmaf(S[kb][r], sl2, -lse_l2));
+        const float p1 = fast_exp2(__builtin_fmaf(S[kb][r + 1], sl2, -lse_l2));
+        ds.x = ok0 ? p0 * (dP[kb][r] - delta) : 0.f;
+        ds.y = ok1 ? p1 * (dP[kb][r + 1] - delta) : 0.f;
+        const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
+        const int slot = 4 * (kb & 1) + r;
+        DS[kb >> 1][slot] = db2.x;
+        DS[kb >> 1][slot + 1] = db2.y;
+      }
+
+    // dQ^T += K^T dS^T (rows = d, columns = queries)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int d4 = 0; d4 < NDB; d4 += 4) {
+        bf16x8_t top[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + 32 * p * D + voff[0][d4 + i]));
+          const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + 32 * p * D + voff[1][d4 + i]));
+          top[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dQacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(top[i], DS[p], dQacc[d4 + i], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+    e = e_n;
+    kt = kt_n;
+    en = en_n;
+    buf ^= 1;
+  }
+
+  const int ge = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) >> 4;
+  if (q_row < L) {
+    const float c = a.scale;
+    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = db * 16 + 4 * ge;
+      f32x4_t v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = dQacc[db][r] * c;
+      if constexpr (OUT_F32) *(f32x4_t*)((float*)a.dq + out_off + d0) = v;
+      else *(bf16x4_t*)((__bf16*)a.dq + out_off + d0) = __builtin_convertvector(v, bf16x4_t);
+    }
+    if (ge == 0) a.delta[bhL + q_row] = delta;
+  }
+}
+
+// ---- dK, dV -------------------------------------------------------------------
+
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int NL = 2 * TileLoadPlan<kBwdWaves, D>::NI;
+  __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int ktile = a.cols.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t bhL = (int64_t)bh * L;
+  const uint16_t* Qg = (const uint16_t*)a.q + in_off;
+  const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
+  const int k_row = ktile * BM + wave * 16 + j16;
+
+  // K, V of this lane's key as B operands (k-step ks: d = 32ks + 8g ..)
+  bf16x8_t Kr[NKS], Vr[NKS];
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const uint16_t* Kg = (const uint16_t*)a.k + in_off;
+    const uint16_t* Vg = (const uint16_t*)a.v + in_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int64_t off = k_row * a.isl + ks * 32 + 8 * g;
+      Kr[ks] = as_bf16x8(k_row < L ? *(const u32x4_t*)(Kg + off) : zero);
+      Vr[ks] = as_bf16x8(k_row < L ? *(const u32x4_t*)(Vg + off) : zero);
+    }
+  }
+  wait_vmcnt<0>();
+
+  const TileLoadPlan<kBwdWaves, D> plan(a.isl, wave, lane, swz_q16<D>);
+  // Q, dO rows of query tile qti; wave 1 brings their lse and D, wave 0 the
+  // key bitmasks of a partial tile
+  auto prefetch = [&](int b, const Entry& x, int qti) {
+    const int row0 = qti * BN;
+    issue_pair_loads<D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
+    if (wave == 1) {
+      const int nrec = min(L - row0, BN) * 4;
+      lds_dma_4(lds_addr(s.rowv[b][0]), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
+      lds_dma_4(lds_addr(s.rowv[b][1]), uint32_t(lane) * 4u, make_rsrc(a.delta + bhL + row0, nrec));
+    }
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.cols.bits, x.pidx, lane);
+  };
+  auto wait_all_but = [&](const Entry& x) {
+    if (wave == 1) wait_vmcnt<NL + 2>();
+    else if (x.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
+    else wait_vmcnt<NL>();
+  };
+  const int e0 = a.cols.qt_off[ktile], e1 = a.cols.qt_off[ktile + 1];
+  int e = e0, qtl = 0;
+  Entry en = {0, 0, -1, 0};
+  if (e < e1) {
+    en = a.cols.entries[e];
+    qtl = en.kt0;
+    prefetch(0, en, qtl);
+  }
+
+  f32x4_t dKacc[NDB], dVacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dKacc[db][r] = dVacc[db][r] = 0.f;
+  const float sl2 = a.scale_log2;
+
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
+  const int vrow = 4 * g + (j16 >> 2);
+  int voff[2][NDB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow + 16 * h;
+      const int chunk = 2 * db + ((j16 & 3) >> 1);
+      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
+    }
+
+  int buf = 0;
+  while (e < e1) {
+    int e_n = e, qt_n = qtl + 1;
+    Entry en_n = en;
+    if (qt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.cols.entries[e_n];
+        qt_n = en_n.kt0;
+      }
+    }
+    if (e_n < e1) {
+      prefetch(buf ^ 1, en_n, qt_n);
+      wait_all_but(en_n);
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const uint16_t* Qt = s.t[buf][0];
+    const uint16_t* dOt = s.t[buf][1];
+
+    // S = Q K^T and dP = dO V^T for the 64 queries of the tile (16-query
+    // blocks qb; lane holds queries 16qb + 4g + r of key j16)
+    f32x4_t S[4], dP[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[qb][r] = dP[qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8_t qop[4], dop[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const int off = qb * 16 * D + koff[ks];
+        qop[qb] = as_bf16x8(*(const u32x4_t*)(Qt + off));
+        dop[qb] = as_bf16x8(*(const u32x4_t*)(dOt + off));
+      }
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[qb], Kr[ks], S[qb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+        dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop[qb], Vr[ks], dP[qb], 0, 0, 0);
+    }
+
+    uint64_t bits = ~0ull;
+    if (en.pidx >= 0) bits = s.bits[buf][wave * 16 + j16] >> (4 * g);
+    bf16x8_t P[2], DS[2];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][16 * qb + 4 * g]);
+      const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][16 * qb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const bool ok0 = (bits >> (16 * qb + r)) & 1ull, ok1 = (bits >> (16 * qb + r + 1)) & 1ull;
+        const float p0 = fast_exp2(__builtin_fmaf(S[qb][r], sl2, -lse4[r] * kLog2e));
+        const float p1 = fast_exp2(__builtin_fmaf(S[qb][r + 1], sl2, -lse4[r + 1] * kLog2e));
+        f32x2_t pv, ds;
+        pv.x = ok0 ? p0 : 0.f;
+        pv.y = ok1 ? p1 : 0.f;
+        ds.x = pv.x * (dP[qb][r] - del4[r]);
+        ds.y = pv.y * (dP[qb][r + 1] - del4[r + 1]);
+        const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
+        const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
+        const int slot = 4 * (qb & 1) + r;
+        P[qb >> 1][slot] = pb.x;
+        P[qb >> 1][slot + 1] = pb.y;
+        DS[qb >> 1][slot] = db2.x;
+        DS[qb >> 1][slot + 1] = db2.y;
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (rows = d, columns = keys)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int d4 = 0; d4 < NDB; d4 += 4) {
+        bf16x8_t oop[4], qtop[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int off_a = 32 * p * D + voff[0][d4 + i];
+          const int off_b = 32 * p * D + voff[1][d4 + i];
+          const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_a));
+          const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_b));
+          const s16x4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Qt + off_a));
+          const s16x4_t y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Qt + off_b));
+          oop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          qtop[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dVacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oop[i], P[p], dVacc[d4 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dKacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtop[i], DS[p], dKacc[d4 + i], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    e = e_n;
+    qtl = qt_n;
+    en = en_n;
+    buf ^= 1;
+  }
+
+  const int ge = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) >> 4;
+  if (k_row < L) {
+    const float c = a.scale;
+    const int64_t out_off = bb * a.osb + hh * a.osh + k_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = db * 16 + 4 * ge;
+      f32x4_t kv, vv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kv[r] = dKacc[db][r] * c;
+        vv[r] = dVacc[db][r];
+      }
+      if constexpr (OUT_F32) {
+        *(f32x4_t*)((float*)a.dk + out_off + d0) = kv;
+        *(f32x4_t*)((float*)a.dv + out_off + d0) = vv;
+      } else {
+        *(bf16x4_t*)((__bf16*)a.dk + out_off + d0) = __builtin_convertvector(kv, bf16x4_t);
+        *(bf16x4_t*)((__bf16*)a.dv + out_off + d0) = __builtin_convertvector(vv, bf16x4_t);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <int D, bool OUT_F32>
+static void launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  const dim3 block(64 * kBwdWaves);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_row_tasks) * a.B * a.H)), block, 0,
+                     stream, a);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_col_tasks) * a.B * a.H)), block, 0,
+                     stream, a);
+}
+
+int launch_bwd(const BwdArgs& a, int out_dtype, int head_dim, hipStream_t stream) {
+  const int64_t g1 = int64_t(a.n_row_tasks) * a.B * a.H, g2 = int64_t(a.n_col_tasks) * a.B * a.H;
+  if (g1 <= 0 || g2 <= 0 || g1 > 0x7fffffff || g2 > 0x7fffffff) return AJ_EINVAL;
+  const bool f32 = out_dtype == AJ_F32;
+  if (head_dim == 128) {
+    if (f32) launch_bwd_d<128, true>(a, stream);
+    else launch_bwd_d<128, false>(a, stream);
+  } else {
+    if (f32) launch_bwd_d<64, true>(a, stream);
+    else launch_bwd_d<64, false>(a, stream);
+  }
+  return hipGetLastError() == hipSuccess ? AJ_OK : AJ_EHIP;
+}
+
+}  // namespace aj

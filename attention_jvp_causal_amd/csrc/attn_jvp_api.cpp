@@ -34,17 +34,26 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
     return AJ_OK;
   }
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t n_off = d->qt_off.size() * sizeof(int32_t);
-  const size_t n_ent = std::max<size_t>(1, d->entries.size()) * sizeof(Entry);
-  const size_t n_task = d->tasks.size() * sizeof(int32_t);
-  const size_t n_bits = std::max<size_t>(1, d->bits.size()) * sizeof(uint64_t);
-  const size_t o_ent = align(n_off), o_task = o_ent + align(n_ent), o_bits = o_task + align(n_task);
-  const size_t total = o_bits + align(n_bits);
+  // layout: [rows map | cols map], each {qt_off | entries | tasks | bits}
+  struct Part {
+    const void* src;
+    size_t bytes, off;
+  };
+  std::vector<Part> parts;
+  size_t total = 0;
+  auto add = [&](const void* src, size_t bytes) {
+    parts.push_back(Part{src, bytes, total});
+    total += align(std::max<size_t>(bytes, 16));
+  };
+  for (const aj::TileMap* m : {&d->rows, &d->cols}) {
+    add(m->qt_off.data(), m->qt_off.size() * sizeof(int32_t));
+    add(m->entries.data(), m->entries.size() * sizeof(Entry));
+    add(m->tasks.data(), m->tasks.size() * sizeof(int32_t));
+    add(m->bits.data(), m->bits.size() * sizeof(uint64_t));
+  }
   std::vector<uint8_t> host(total, 0);
-  std::memcpy(host.data(), d->qt_off.data(), n_off);
-  if (!d->entries.empty()) std::memcpy(host.data() + o_ent, d->entries.data(), d->entries.size() * sizeof(Entry));
-  std::memcpy(host.data() + o_task, d->tasks.data(), n_task);
-  if (!d->bits.empty()) std::memcpy(host.data() + o_bits, d->bits.data(), d->bits.size() * sizeof(uint64_t));
+  for (const Part& x : parts)
+    if (x.bytes) std::memcpy(host.data() + x.off, x.src, x.bytes);
   void* base = nullptr;
   if (hipMalloc(&base, total) != hipSuccess) return AJ_ENOMEM;
   if (hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
@@ -52,10 +61,13 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
     return AJ_EHIP;
   }
   uint8_t* b = static_cast<uint8_t*>(base);
-  t.qt_off = reinterpret_cast<const int32_t*>(b);
-  t.entries = reinterpret_cast<const Entry*>(b + o_ent);
-  t.tasks = reinterpret_cast<const int32_t*>(b + o_task);
-  t.bits = reinterpret_cast<const uint64_t*>(b + o_bits);
+  aj::DeviceMap* dm[2] = {&t.rows, &t.cols};
+  for (int i = 0; i < 2; ++i) {
+    dm[i]->qt_off = reinterpret_cast<const int32_t*>(b + parts[4 * i].off);
+    dm[i]->entries = reinterpret_cast<const Entry*>(b + parts[4 * i + 1].off);
+    dm[i]->tasks = reinterpret_cast<const int32_t*>(b + parts[4 * i + 2].off);
+    dm[i]->bits = reinterpret_cast<const uint64_t*>(b + parts[4 * i + 3].off);
+  }
   t.base = base;
   *out = &t;
   return AJ_OK;
@@ -121,10 +133,10 @@ int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void*
   r.isb = s->in_stride_b; r.ish = s->in_stride_h; r.isl = s->in_stride_l;
   r.osb = s->out_stride_b; r.osh = s->out_stride_h; r.osl = s->out_stride_l;
   r.B = s->batch; r.H = s->heads; r.L = s->seq_len;
-  r.n_tasks = mask->n_qt;
+  r.n_tasks = mask->rows.n_qt;
   r.scale = scale;
   r.scale_log2 = float(double(scale) * 1.4426950408889634074);
-  r.qt_off = t->qt_off; r.entries = t->entries; r.tasks = t->tasks; r.bits = t->bits;
+  r.qt_off = t->rows.qt_off; r.entries = t->rows.entries; r.tasks = t->rows.tasks; r.bits = t->rows.bits;
   return AJ_OK;
 }
 
@@ -187,7 +199,7 @@ int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t*
 
 int32_t attn_jvp_mask_desc_work(const aj_mask_desc* d, int64_t* pairs_by_variant) {
   if (!d || !pairs_by_variant) return AJ_EINVAL;
-  for (int i = 0; i < 3; ++i) pairs_by_variant[i] = d->pairs_by_var[i];
+  for (int i = 0; i < 3; ++i) pairs_by_variant[i] = d->rows.pairs_by_var[i];
   return AJ_OK;
 }
 
@@ -197,43 +209,55 @@ int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* d, aj_mask_stats* s) {
   s->seq_len = d->seq_len;
   s->tile_m = d->tile_m;
   s->tile_n = d->tile_n;
-  s->num_q_tiles = d->n_qt;
-  s->num_k_tiles = d->n_kt;
-  s->full_tiles = d->full_tiles;
-  s->partial_tiles = d->partial_tiles;
-  s->num_entries = int32_t(d->entries.size());
+  s->num_q_tiles = d->rows.n_qt;
+  s->num_k_tiles = d->rows.n_kt;
+  s->full_tiles = d->rows.full_tiles;
+  s->partial_tiles = d->rows.partial_tiles;
+  s->num_entries = int32_t(d->rows.entries.size());
   return AJ_OK;
 }
 
-static const Entry* find_entry(const aj_mask_desc* d, int32_t qt, int32_t kt) {
-  for (int32_t e = d->qt_off[qt]; e < d->qt_off[qt + 1]; ++e)
-    if (d->entries[e].kt0 <= kt && kt < d->entries[e].kt1) return &d->entries[e];
+static const Entry* find_entry(const aj::TileMap& m, int32_t qt, int32_t kt) {
+  for (int32_t e = m.qt_off[qt]; e < m.qt_off[qt + 1]; ++e)
+    if (m.entries[e].kt0 <= kt && kt < m.entries[e].kt1) return &m.entries[e];
   return nullptr;
 }
 
 int32_t attn_jvp_mask_desc_tile_kind(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t* kind) {
-  if (!d || !kind || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt) return AJ_EINVAL;
-  const Entry* e = find_entry(d, qt, kt);
+  if (!d || !kind || qt < 0 || qt >= d->rows.n_qt || kt < 0 || kt >= d->rows.n_kt) return AJ_EINVAL;
+  const Entry* e = find_entry(d->rows, qt, kt);
   *kind = !e ? 0 : (e->pidx >= 0 ? 1 : 2);
   return AJ_OK;
 }
 
 int32_t attn_jvp_mask_desc_tile_variant(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t* variant) {
-  if (!d || !variant || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt) return AJ_EINVAL;
-  const Entry* e = find_entry(d, qt, kt);
+  if (!d || !variant || qt < 0 || qt >= d->rows.n_qt || kt < 0 || kt >= d->rows.n_kt) return AJ_EINVAL;
+  const Entry* e = find_entry(d->rows, qt, kt);
   *variant = !e ? -1 : e->flags;
+  return AJ_OK;
+}
+
+// Bitmask of one owner row of tile (ot, vt) in map m (see row_bits).
+static int32_t map_bits(const aj::TileMap& m, int32_t L, int32_t ot, int32_t vt, int32_t row, uint64_t* bits) {
+  if (!bits || ot < 0 || ot >= m.n_qt || vt < 0 || vt >= m.n_kt || row < 0 || row >= aj::kTileM)
+    return AJ_EINVAL;
+  const Entry* e = find_entry(m, ot, vt);
+  if (!e || ot * aj::kTileM + row >= L) *bits = 0;
+  else if (e->pidx < 0) *bits = ~0ull;
+  else *bits = m.bits[size_t(e->pidx) * aj::kTileM + row];
   return AJ_OK;
 }
 
 int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* d, int32_t qt, int32_t kt, int32_t row,
                                     uint64_t* bits) {
-  if (!d || !bits || qt < 0 || qt >= d->n_qt || kt < 0 || kt >= d->n_kt || row < 0 || row >= d->tile_m)
-    return AJ_EINVAL;
-  const Entry* e = find_entry(d, qt, kt);
-  if (!e || qt * d->tile_m + row >= d->seq_len) *bits = 0;
-  else if (e->pidx < 0) *bits = ~0ull;
-  else *bits = d->bits[size_t(e->pidx) * d->tile_m + row];
-  return AJ_OK;
+  if (!d) return AJ_EINVAL;
+  return map_bits(d->rows, d->seq_len, qt, kt, row, bits);
+}
+
+int32_t attn_jvp_mask_desc_col_bits(const aj_mask_desc* d, int32_t k_tile, int32_t q_tile, int32_t key_row,
+                                    uint64_t* bits) {
+  if (!d) return AJ_EINVAL;
+  return map_bits(d->cols, d->seq_len, k_tile, q_tile, key_row, bits);
 }
 
 void attn_jvp_mask_desc_free(aj_mask_desc* d) {
@@ -257,7 +281,7 @@ int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void
   int32_t st = prepare(s, ins, 6, outs, 3, mask, scale, &a);
   if (st != AJ_OK) return st;
   a.tq = tq; a.tk = tk; a.tv = tv; a.to = to;
-  const bool variants = mask->pairs_by_var[1] + mask->pairs_by_var[2] > 0;
+  const bool variants = mask->rows.pairs_by_var[1] + mask->rows.pairs_by_var[2] > 0;
   return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, true, variants,
                         static_cast<hipStream_t>(stream));
 }
@@ -274,6 +298,35 @@ int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v,
   a.to = nullptr;
   return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, false, false,
                         static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, const aj_mask_desc* mask, float scale, void* dq, void* dk, void* dv,
+                 float* delta, void* stream) {
+  const void* ins[5] = {q, k, v, o, dout};
+  const void* outs[4] = {dq, dk, dv, delta};
+  aj::FwdArgs f;
+  int32_t st = prepare(s, ins, 5, outs, 4, mask, scale, &f);
+  if (st != AJ_OK) return st;
+  if (!lse || !aligned16(lse)) return AJ_EINVAL;
+  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
+  const DeviceTables* t = nullptr;
+  st = device_tables(mask, &t);
+  if (st != AJ_OK) return st;
+  aj::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
+  a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.isb = f.isb; a.ish = f.ish; a.isl = f.isl;
+  a.osb = f.osb; a.osh = f.osh; a.osl = f.osl;
+  a.B = f.B; a.H = f.H; a.L = f.L;
+  a.n_row_tasks = mask->rows.n_qt;
+  a.n_col_tasks = mask->cols.n_qt;
+  a.scale = f.scale;
+  a.scale_log2 = f.scale_log2;
+  a.rows = t->rows;
+  a.cols = t->cols;
+  return aj::launch_bwd(a, s->out_dtype, s->head_dim, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // Host-side mask descriptor: frame-level layouts -> admissible rectangles ->
-// tile-level skip / partial / full map -> longest-first task list.
+// tile-level skip / partial / full maps (by query tile, and by key tile for
+// the key-parallel gradient kernel) -> longest-first task lists.
 //
 // "Causal-rCM", App. B ("Sparse custom-mask representation"): the custom mask
 // is a set of query groups, each a contiguous query interval with a list of
@@ -117,6 +118,122 @@ int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out
   return AJ_OK;
 }
 
+// Tile map of rectangles r (owner axis first: {o0, o1, v0, v1}) with owner
+// tiles of kTileM and visited tiles of kTileN.  tfree (merged ranges) marks
+// tangent-free tokens; both axes index the same sequence.
+static void build_map(int32_t L, const int32_t* r, int32_t n, const std::vector<int32_t>& tfree, TileMap* m) {
+  const int32_t BM = kTileM, BN = kTileN;
+  m->n_qt = (L + BM - 1) / BM;
+  m->n_kt = (L + BN - 1) / BN;
+  // tangent-free owner and visited tiles: every token of the tile inside
+  // [0, L) is declared tangent-free
+  auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(L, qt * BM + BM)); };
+  auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(L, kt * BN + BN)); };
+  auto variant = [&](bool qf, int32_t kt) {
+    return k_free(kt) ? (qf ? kTileAllFree : kTileKeysFree) : kTileJvp;
+  };
+
+  // bucket rectangles by the owner tiles they touch
+  std::vector<std::vector<RectRef>> per_qt(m->n_qt);
+  for (int32_t i = 0; i < n; ++i) {
+    RectRef x{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+    for (int32_t qt = x.q0 / BM; qt <= (x.q1 - 1) / BM; ++qt) per_qt[qt].push_back(x);
+  }
+
+  std::vector<int64_t> work(m->n_qt, 0);
+  m->qt_off.assign(m->n_qt + 1, 0);
+  for (int32_t qt = 0; qt < m->n_qt; ++qt) {
+    m->qt_off[qt] = int32_t(m->entries.size());
+    const bool qf = q_free(qt);
+    const int32_t a = qt * BM, b = std::min(L, a + BM);
+    const int64_t full_count = int64_t(b - a) * BN;  // allowed pairs in a full tile
+    // allowed-pair count per visited tile: runs of interior tiles go into a
+    // difference map, the (at most two) boundary tiles of each rectangle
+    // into a point map
+    std::map<int32_t, int64_t> run_delta, points;
+    for (const RectRef& x : per_qt[qt]) {
+      const int64_t rows = std::min(b, x.q1) - std::max(a, x.q0);
+      const int32_t kf = x.k0 / BN, kl = (x.k1 - 1) / BN;
+      if (kf == kl) {
+        points[kf] += rows * (x.k1 - x.k0);
+        continue;
+      }
+      points[kf] += rows * (int64_t(kf + 1) * BN - x.k0);
+      points[kl] += rows * (x.k1 - int64_t(kl) * BN);
+      if (kl > kf + 1) {
+        run_delta[kf + 1] += rows * BN;
+        run_delta[kl] -= rows * BN;
+      }
+    }
+    // sweep over breakpoints in visited-tile order
+    std::vector<int32_t> cuts;
+    for (auto& kv : run_delta) cuts.push_back(kv.first);
+    for (auto& kv : points) {
+      cuts.push_back(kv.first);
+      cuts.push_back(kv.first + 1);
+    }
+    std::sort(cuts.begin(), cuts.end());
+    cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+    int64_t run = 0;
+    auto rd = run_delta.begin();
+    for (size_t ci = 0; ci + 1 < cuts.size(); ++ci) {
+      const int32_t s0 = cuts[ci], s1 = cuts[ci + 1];
+      while (rd != run_delta.end() && rd->first <= s0) run += (rd++)->second;
+      auto pt = points.find(s0);
+      const bool is_point = pt != points.end();
+      const int64_t cnt = run + (is_point ? pt->second : 0);
+      // cuts include p and p + 1 for every point tile p, so a point segment
+      // is exactly one tile wide
+      const int32_t e1 = s1;
+      if (cnt == 0) continue;
+      const bool in_range = int64_t(e1) * BN <= L;
+      if (cnt == full_count && in_range) {
+        for (int32_t kt = s0; kt < e1; ++kt) {
+          const int32_t fl = variant(qf, kt);
+          if (int32_t(m->entries.size()) > m->qt_off[qt] && m->entries.back().pidx < 0 &&
+              m->entries.back().kt1 == kt && m->entries.back().flags == fl)
+            m->entries.back().kt1 = kt + 1;  // extend the previous full run
+          else
+            m->entries.push_back(Entry{kt, kt + 1, -1, fl});
+          m->pairs_by_var[var_index(fl)] += full_count;
+        }
+        m->full_tiles += e1 - s0;
+      } else {
+        for (int32_t kt = s0; kt < e1; ++kt) {
+          const int32_t pidx = m->partial_tiles++;
+          const int32_t fl = variant(qf, kt);
+          m->entries.push_back(Entry{kt, kt + 1, pidx, fl});
+          m->bits.resize(size_t(m->partial_tiles) * BM, 0);
+          uint64_t* rowbits = &m->bits[size_t(pidx) * BM];
+          const int32_t key0 = kt * BN;
+          for (const RectRef& x : per_qt[qt]) {
+            const int32_t kk0 = std::max(x.k0, key0), kk1 = std::min(x.k1, key0 + BN);
+            if (kk0 >= kk1) continue;
+            const int32_t w = kk1 - kk0;
+            const uint64_t msk = (w == 64 ? ~0ull : ((1ull << w) - 1)) << (kk0 - key0);
+            for (int32_t q = std::max(a, x.q0); q < std::min(b, x.q1); ++q) rowbits[q - a] |= msk;
+          }
+          int64_t c = 0;
+          for (int32_t row = 0; row < BM; ++row) c += __builtin_popcountll(rowbits[row]);
+          m->pairs_by_var[var_index(fl)] += c;
+        }
+      }
+    }
+    for (int32_t e = m->qt_off[qt]; e < int32_t(m->entries.size()); ++e)
+      work[qt] += (m->entries[e].kt1 - m->entries[e].kt0) * tile_cost(m->entries[e].flags);
+  }
+  m->qt_off[m->n_qt] = int32_t(m->entries.size());
+
+  // tasks: every owner tile (tiles with nothing allowed still write zeros),
+  // most work first (visited tiles weighted by their variant's cost); ties by
+  // larger tile index
+  m->tasks.resize(m->n_qt);
+  for (int32_t qt = 0; qt < m->n_qt; ++qt) m->tasks[qt] = qt;
+  std::stable_sort(m->tasks.begin(), m->tasks.end(), [&](int32_t x, int32_t y) {
+    return work[x] != work[y] ? work[x] > work[y] : x > y;
+  });
+}
+
 int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,
                          const int32_t* tf, int32_t n_tf, aj_mask_desc** out) {
   if (!out) return AJ_EINVAL;
@@ -132,122 +249,22 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
   aj_mask_desc* d = new (std::nothrow) aj_mask_desc();
   if (!d) return AJ_ENOMEM;
   try {
-    const int32_t BM = kTileM, BN = kTileN;
     d->seq_len = L;
     d->head_dim = head_dim;
     d->dtype = dtype;
-    d->n_qt = (L + BM - 1) / BM;
-    d->n_kt = (L + BN - 1) / BN;
     d->rects.assign(r, r + 4 * size_t(n));
     d->tfree = tfree;
-    // tangent-free query and key tiles: every token of the tile inside [0, L)
-    // is declared tangent-free
-    auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(L, qt * BM + BM)); };
-    auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(L, kt * BN + BN)); };
-    auto variant = [&](bool qf, int32_t kt) {
-      return k_free(kt) ? (qf ? kTileAllFree : kTileKeysFree) : kTileJvp;
-    };
-
-    // bucket rectangles by the query tiles they touch
-    std::vector<std::vector<RectRef>> per_qt(d->n_qt);
+    for (int32_t i = 0; i < n; ++i) d->pairs += int64_t(r[4 * i + 1] - r[4 * i]) * (r[4 * i + 3] - r[4 * i + 2]);
+    build_map(L, r, n, tfree, &d->rows);
+    // the transposed mask: key tiles own runs of query tiles (no variants)
+    std::vector<int32_t> tr(4 * size_t(n));
     for (int32_t i = 0; i < n; ++i) {
-      RectRef x{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
-      d->pairs += int64_t(x.q1 - x.q0) * (x.k1 - x.k0);
-      for (int32_t qt = x.q0 / BM; qt <= (x.q1 - 1) / BM; ++qt) per_qt[qt].push_back(x);
+      tr[4 * i] = r[4 * i + 2];
+      tr[4 * i + 1] = r[4 * i + 3];
+      tr[4 * i + 2] = r[4 * i];
+      tr[4 * i + 3] = r[4 * i + 1];
     }
-
-    std::vector<int64_t> work(d->n_qt, 0);
-    d->qt_off.assign(d->n_qt + 1, 0);
-    for (int32_t qt = 0; qt < d->n_qt; ++qt) {
-      d->qt_off[qt] = int32_t(d->entries.size());
-      const bool qf = q_free(qt);
-      const int32_t a = qt * BM, b = std::min(L, a + BM);
-      const int64_t full_count = int64_t(b - a) * BN;  // allowed pairs in a full tile
-      // allowed-pair count per key tile: runs of interior tiles go into a
-      // difference map, the (at most two) boundary tiles of each rectangle
-      // into a point map
-      std::map<int32_t, int64_t> run_delta, points;
-      for (const RectRef& x : per_qt[qt]) {
-        const int64_t rows = std::min(b, x.q1) - std::max(a, x.q0);
-        const int32_t kf = x.k0 / BN, kl = (x.k1 - 1) / BN;
-        if (kf == kl) {
-          points[kf] += rows * (x.k1 - x.k0);
-          continue;
-        }
-        points[kf] += rows * (int64_t(kf + 1) * BN - x.k0);
-        points[kl] += rows * (x.k1 - int64_t(kl) * BN);
-        if (kl > kf + 1) {
-          run_delta[kf + 1] += rows * BN;
-          run_delta[kl] -= rows * BN;
-        }
-      }
-      // sweep over breakpoints in key-tile order
-      std::vector<int32_t> cuts;
-      for (auto& kv : run_delta) cuts.push_back(kv.first);
-      for (auto& kv : points) {
-        cuts.push_back(kv.first);
-        cuts.push_back(kv.first + 1);
-      }
-      std::sort(cuts.begin(), cuts.end());
-      cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
-      int64_t run = 0;
-      auto rd = run_delta.begin();
-      for (size_t ci = 0; ci + 1 < cuts.size(); ++ci) {
-        const int32_t s0 = cuts[ci], s1 = cuts[ci + 1];
-        while (rd != run_delta.end() && rd->first <= s0) run += (rd++)->second;
-        auto pt = points.find(s0);
-        const bool is_point = pt != points.end();
-        const int64_t cnt = run + (is_point ? pt->second : 0);
-        // cuts include p and p + 1 for every point tile p, so a point segment
-        // is exactly one tile wide
-        const int32_t e1 = s1;
-        if (cnt == 0) continue;
-        const bool in_range = int64_t(e1) * BN <= L;
-        if (cnt == full_count && in_range) {
-          for (int32_t kt = s0; kt < e1; ++kt) {
-            const int32_t fl = variant(qf, kt);
-            if (int32_t(d->entries.size()) > d->qt_off[qt] && d->entries.back().pidx < 0 &&
-                d->entries.back().kt1 == kt && d->entries.back().flags == fl)
-              d->entries.back().kt1 = kt + 1;  // extend the previous full run
-            else
-              d->entries.push_back(Entry{kt, kt + 1, -1, fl});
-            d->pairs_by_var[var_index(fl)] += full_count;
-          }
-          d->full_tiles += e1 - s0;
-        } else {
-          for (int32_t kt = s0; kt < e1; ++kt) {
-            const int32_t pidx = d->partial_tiles++;
-            const int32_t fl = variant(qf, kt);
-            d->entries.push_back(Entry{kt, kt + 1, pidx, fl});
-            d->bits.resize(size_t(d->partial_tiles) * BM, 0);
-            uint64_t* rowbits = &d->bits[size_t(pidx) * BM];
-            const int32_t key0 = kt * BN;
-            for (const RectRef& x : per_qt[qt]) {
-              const int32_t kk0 = std::max(x.k0, key0), kk1 = std::min(x.k1, key0 + BN);
-              if (kk0 >= kk1) continue;
-              const int32_t w = kk1 - kk0;
-              const uint64_t m = (w == 64 ? ~0ull : ((1ull << w) - 1)) << (kk0 - key0);
-              for (int32_t q = std::max(a, x.q0); q < std::min(b, x.q1); ++q) rowbits[q - a] |= m;
-            }
-            int64_t c = 0;
-            for (int32_t row = 0; row < BM; ++row) c += __builtin_popcountll(rowbits[row]);
-            d->pairs_by_var[var_index(fl)] += c;
-          }
-        }
-      }
-      for (int32_t e = d->qt_off[qt]; e < int32_t(d->entries.size()); ++e)
-        work[qt] += (d->entries[e].kt1 - d->entries[e].kt0) * tile_cost(d->entries[e].flags);
-    }
-    d->qt_off[d->n_qt] = int32_t(d->entries.size());
-
-    // tasks: every query tile (tiles with no allowed key still write zeros),
-    // most work first (visited key tiles weighted by their variant's cost);
-    // ties by larger tile index
-    d->tasks.resize(d->n_qt);
-    for (int32_t qt = 0; qt < d->n_qt; ++qt) d->tasks[qt] = qt;
-    std::stable_sort(d->tasks.begin(), d->tasks.end(), [&](int32_t x, int32_t y) {
-      return work[x] != work[y] ? work[x] > work[y] : x > y;
-    });
+    build_map(L, tr.data(), n, std::vector<int32_t>(), &d->cols);
   } catch (const std::bad_alloc&) {
     delete d;
     return AJ_ENOMEM;

@@ -13,7 +13,10 @@ Other measurements of the same kernels (one JSON line each, same schema):
                    tangent-free: `value` stays in the 12d convention (the work
                    of the plain JVP), the roofline counts the FLOPs executed
                    (12d / 8d / 4d per pair by tile class);
-  --op fwd         primal masked attention (O, lse): 4d FLOP per pair.
+  --op fwd         primal masked attention (O, lse): 4d FLOP per pair;
+  --op bwd         its gradients (dq, dk, dv from o, lse, dO): 10d FLOP per pair
+                   by the usual count of five products (the kernels execute 14d:
+                   the scores and dP are formed once per kernel).
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
@@ -36,16 +39,19 @@ PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak, 1 GPU"
 METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", "attn_jvp_fwd.hip")
+METRIC_BWD = "masked attention backward TFLOP/s (unmasked FLOPs, 10d per pair) and % of bf16 MFMA peak, 1 GPU"
+KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n) for n in ("aj_device.h", "attn_jvp_fwd.hip")]
 
 
 def kernel_sha() -> str:
-    """Hash of the kernel source with comments and blank lines removed, so that
-    a counter record stays valid across comment-only edits."""
+    """Hash of the JVP kernel's sources with comments and blank lines removed,
+    so that a counter record stays valid across comment-only edits."""
     import re
 
-    with open(KERNEL_SRC) as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            src += f.read()
     src = re.sub(r"//[^\n]*", "", src)
     code = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
@@ -164,8 +170,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=None, help="workload name (default: the c3-3 Wan2.1-1.3B shape)")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads timed for the oracle baseline (0 = skip)")
-    ap.add_argument("--op", default="jvp", choices=["jvp", "fwd"],
-                    help="jvp: O, tO, lse (the metric); fwd: primal O, lse only")
+    ap.add_argument("--op", default="jvp", choices=["jvp", "fwd", "bwd"],
+                    help="jvp: O, tO, lse (the metric); fwd: primal O, lse only; bwd: dq, dk, dv")
     ap.add_argument("--tangent-free", action="store_true",
                     help="declare the clean half of a teacher-forcing workload tangent-free")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -204,12 +210,15 @@ def main(argv=None):
             raise SystemExit(f"--tangent-free needs a workload whose clean half has zero tangents, not {w.name}")
         desc = aj.attn_jvp_mask_desc_tangent_free(desc, [(0, w.seq_len // 2)])
     pairs = desc.unmasked_pairs * w.batch * w.heads
-    per_pair = 12.0 if args.op == "jvp" else 4.0
+    per_pair = {"jvp": 12.0, "fwd": 4.0, "bwd": 10.0}[args.op]
     flop = per_pair * w.head_dim * pairs
-    # FLOPs the kernel executes: fewer than the convention's on tangent-free tiles
+    # FLOPs the kernels execute: fewer than the convention's on tangent-free
+    # tiles; more for the gradients (14d)
     if args.op == "jvp":
         wk = desc.work()
         exec_flop = float(w.head_dim) * w.batch * w.heads * (12.0 * wk[0] + 8.0 * wk[1] + 4.0 * wk[2])
+    elif args.op == "bwd":
+        exec_flop = 14.0 * w.head_dim * pairs
     else:
         exec_flop = flop
     out_dtype = {None: None, "bf16": torch.bfloat16, "f32": torch.float32}[args.out_dtype]
@@ -220,11 +229,21 @@ def main(argv=None):
             torch.empty((B, H, L), dtype=torch.float32, device="cuda:0"))
     args_ = [dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")]
 
+    if args.op == "bwd":
+        # forward outputs and a cotangent, made before the timed region
+        o_f, lse_f = aj.attn_fwd(*args_[:3], desc, scale=w.scale)
+        g = torch.Generator().manual_seed(1234)
+        d_out = torch.randn(w.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to("cuda:0")
+        grads = tuple(torch.empty((B, H, L, D), dtype=odt, device="cuda:0") for _ in range(3)) + (
+            torch.empty((B, H, L), dtype=torch.float32, device="cuda:0"),)
+
     def step():
         if args.op == "jvp":
             aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
-        else:
+        elif args.op == "fwd":
             aj.attn_fwd(*args_[:3], desc, scale=w.scale, out_dtype=out_dtype, out=(outs[0], outs[2]))
+        else:
+            aj.attn_bwd(*args_[:3], o_f, d_out, lse_f, desc, scale=w.scale, out_dtype=out_dtype, out=grads)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -256,8 +275,8 @@ def main(argv=None):
     achieved = exec_flop / (avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     traffic = measured_traffic(w.name)
-    n_in, n_out = (6, 2) if args.op == "jvp" else (3, 1)
-    in_bytes = n_in * B * H * L * D * inputs["q"].element_size()
+    n_in, n_out = {"jvp": (6, 2), "fwd": (3, 1), "bwd": (5, 3)}[args.op]
+    in_bytes = n_in * B * H * L * D * inputs["q"].element_size() + (B * H * L * 4 if args.op == "bwd" else 0)
     out_bytes = n_out * B * H * L * D * odt.itemsize + B * H * L * 4
     if args.op != "jvp" or args.tangent_free:
         traffic = None  # counters are recorded for the plain JVP only
@@ -266,7 +285,7 @@ def main(argv=None):
     if args.cpu_heads > 0 and args.op == "jvp":
         cpu = cpu_baseline(w, inputs, min(args.cpu_heads, w.heads))
 
-    metric = METRIC if args.op == "jvp" else METRIC_FWD
+    metric = {"jvp": METRIC, "fwd": METRIC_FWD, "bwd": METRIC_BWD}[args.op]
     rec = {
         "metric": metric,
         "value": round(value, 2),
@@ -303,7 +322,8 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": kernel_name(w.dtype, D, odt == torch.float32, args.op == "jvp", args.tangent_free),
+            "kernel": (kernel_name(w.dtype, D, odt == torch.float32, args.op == "jvp", args.tangent_free)
+                       if args.op != "bwd" else "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel"),
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,

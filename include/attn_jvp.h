@@ -166,6 +166,13 @@ int32_t attn_jvp_mask_desc_tile_variant(const aj_mask_desc* desc, int32_t q_tile
 int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* desc, int32_t q_tile, int32_t k_tile,
                                     int32_t row, uint64_t* bits);
 
+/* The same mask seen from the keys (the map the key-parallel gradient kernel
+ * walks): bit j set when query q_tile * 64 + j may attend key
+ * k_tile * 128 + key_row.  Key tiles are 128 keys, query tiles 64 queries.
+ * Errors: AJ_EINVAL on null arguments or out-of-range indices. */
+int32_t attn_jvp_mask_desc_col_bits(const aj_mask_desc* desc, int32_t k_tile, int32_t q_tile, int32_t key_row,
+                                    uint64_t* bits);
+
 /* Release a descriptor and its device tables on every device that used it.
  * Must not be called while a launch that uses it may still run.  NULL is a
  * no-op. */
@@ -213,6 +220,26 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
  * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
 int32_t attn_fwd(const aj_shape* shape, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
                  float scale, void* o, float* lse, void* stream);
+
+/* Gradients of masked attention for a cotangent dout: dq, dk, dv of
+ * O = softmax(scale * Q K^T + M) V, the backward of attn_fwd on the same
+ * descriptor (training differentiates the packed teacher-forcing forward,
+ * Sec. 3.1.1, Eq. 8).  With P_ij = exp(scale <q_i, k_j> - lse_i) on allowed
+ * pairs, D_i = <dout_i, o_i> and dS_ij = P_ij (<dout_i, v_j> - D_i):
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i P_ij dout_i.
+ * Inputs q, k, v, o, dout: [B, H, L, D] bf16 sharing the input strides; o
+ * and lse as written by attn_fwd (or attn_jvp_fwd) for the same q, k, v,
+ * descriptor and scale.  Outputs dq, dk, dv: [B, H, L, D] out_dtype sharing
+ * the output strides (fully written; rows no query or key uses get zeros).
+ * delta: [B, H, L] float32, written with D (workspace the caller owns; the
+ * kernels read it back).  Two kernels run in order on `stream`; no atomics,
+ * the result is deterministic.  Same checks as attn_jvp_fwd; in_dtype must be
+ * AJ_BF16 (AJ_ENOTSUP otherwise).  Outputs must not overlap the inputs or
+ * each other.  Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
+int32_t attn_bwd(const aj_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
+                 void* dk, void* dv, float* delta, void* stream);
 
 #ifdef __cplusplus
 }

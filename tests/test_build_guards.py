@@ -14,12 +14,15 @@ from attention_jvp_causal_amd import build as B
 
 
 def _device_asm(tmp_path):
-    out = tmp_path / "k.s"
-    cmd = [B.hipcc(), *B.compile_flags(), "-x", "hip", "-S", "--cuda-device-only",
-           os.path.join(B.CSRC, "attn_jvp_fwd.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return out.read_text()
+    text = []
+    for src in (x for x in B.SOURCES if x.endswith(".hip")):
+        out = tmp_path / (src + ".s")
+        cmd = [B.hipcc(), *B.compile_flags(), "-x", "hip", "-S", "--cuda-device-only",
+               os.path.join(B.CSRC, src), "-o", str(out)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
@@ -28,6 +31,7 @@ def test_m0_only_used_by_the_dma_asm_blocks(tmp_path):
     asm = _device_asm(tmp_path)
     kernels = re.findall(r"^(_ZN2aj\w+kernel\w+):", asm, flags=re.M)
     assert any("bf16" in k for k in kernels) and any("f32" in k for k in kernels)
+    assert any("attn_bwd_dq" in k for k in kernels) and any("attn_bwd_dkdv" in k for k in kernels)
     inside = False
     outside_uses = []
     for line in asm.splitlines():

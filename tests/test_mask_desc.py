@@ -129,3 +129,34 @@ def test_equivalent_rects_give_same_tile_map():
     rects = [(0, 100, 0, 100), (100, 200, 0, 200), (200, 300, 0, 300)]
     b = aj.attn_jvp_mask_desc_from_rects(300, rects, head_dim=128, dtype="bf16")
     assert a.stats() == b.stats()
+
+
+@pytest.mark.parametrize("mask", [
+    MaskLayout("block_causal", 7, 37, 3), MaskLayout("tf_clean_noisy", 4, 45, 1), MaskLayout("full", 3, 70, 1),
+    RectMask(300, ((0, 100, 0, 100), (130, 300, 0, 40), (130, 300, 150, 300))),
+], ids=["c3_ragged", "tf", "full", "rects"])
+def test_column_map_is_the_transposed_mask(mask):
+    # the key-tile map (128 keys x 64 queries) against the element predicate
+    L = mask.seq_len
+    if isinstance(mask, MaskLayout):
+        d = aj.attn_jvp_mask_desc_build(mask.kind, mask.num_frames, mask.frame_tokens, mask.frames_per_chunk,
+                                        head_dim=128, dtype="bf16")
+    else:
+        d = aj.attn_jvp_mask_desc_from_rects(L, mask.rects, head_dim=128, dtype="bf16")
+    dm = dense_mask(mask)
+    nk, nq = -(-L // 128), -(-L // 64)
+    pairs = 0
+    for kt in range(nk):
+        for qt in range(nq):
+            for r in range(128):
+                key = kt * 128 + r
+                want = 0
+                if key < L:
+                    for j in range(64):
+                        q = qt * 64 + j
+                        if q < L and dm[q, key]:
+                            want |= 1 << j
+                got = d.col_bits(kt, qt, r)
+                assert got == want, (kt, qt, r)
+                pairs += bin(got).count("1")
+    assert pairs == unmasked_pairs(mask)
