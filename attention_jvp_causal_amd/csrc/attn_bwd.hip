@@ -34,7 +34,8 @@
 
 namespace aj {
 
-constexpr int kBwdWaves = 8;
+constexpr int kBwdWaves = 8;    // 16-row waves
+constexpr int kDqWaves32 = 4;   // 32-row waves of the dQ kernel
 constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int D>
@@ -43,6 +44,13 @@ struct BwdLds {
   uint16_t t[2][2][TILE];              // [buffer][(K, V) for dQ | (Q, dO) for dK, dV]
   uint64_t bits[2][BM];                // per-row bitmask of a partial tile
   float rowv[2][2][256];               // [buffer][lse, D] of the 64 streamed queries
+};
+
+// K and V tiles only (the 32-row dQ kernel): 66 KB, two workgroups per CU.
+template <int D>
+struct KvLds {
+  uint16_t t[2][2][BN * D];  // [buffer][K, V]
+  uint64_t bits[2][BM];
 };
 
 // One direct buffer -> LDS load of 4 bytes per lane (lane l's dword lands at
@@ -58,19 +66,19 @@ __device__ __forceinline__ void lds_dma_4(uint32_t lds_base, uint32_t voffset, i
 }
 
 // DMA of rows [row0, row0 + BN) of two [L, D] tensors into one LDS buffer.
-template <int D>
-__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<kBwdWaves, D>& plan,
+template <int NW, int D>
+__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* s0, const uint16_t* s1, int64_t sl, int row0, int L,
                                                  int wave) {
   const int nrec = int((int64_t)min(L - row0, BN) * sl * 2);
   const i32x4_t r0 = make_rsrc(s0 + (int64_t)row0 * sl, nrec);
   const i32x4_t r1 = make_rsrc(s1 + (int64_t)row0 * sl, nrec);
 #pragma unroll
-  for (int i = 0; i < TileLoadPlan<kBwdWaves, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[0] + (wave + kBwdWaves * i) * 512), plan.voff[i], r0);
+  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[0] + (wave + NW * i) * 512), plan.voff[i], r0);
 #pragma unroll
-  for (int i = 0; i < TileLoadPlan<kBwdWaves, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[1] + (wave + kBwdWaves * i) * 512), plan.voff[i], r1);
+  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[1] + (wave + NW * i) * 512), plan.voff[i], r1);
 }
 
 __device__ __forceinline__ float bf16_dot8(bf16x8_t x, bf16x8_t y, float acc) {
@@ -128,7 +136,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 
   const TileLoadPlan<kBwdWaves, D> plan(a.isl, wave, lane, swz_q16<D>);
   auto prefetch = [&](int b, const Entry& x, int kti) {
-    issue_pair_loads<D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
+    issue_pair_loads<kBwdWaves, D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.rows.bits, x.pidx, lane);
   };
   const int e0 = a.rows.qt_off[qt], e1 = a.rows.qt_off[qt + 1];
@@ -271,6 +279,182 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// dQ with 32-row waves (v_mfma_f32_32x32x16_bf16): 4 waves own the 128-row
+// query tile and two workgroups share a CU.  Lanes l and l + 32 hold the same
+// query row; S^T, dP^T and dS^T keep the forward q32 kernel's layout, so the
+// K^T transpose reads and the slot order of the B operand are the same.
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqWaves32), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq32_kernel(BwdArgs a) {
+  constexpr int NKK = D / 16;  // MFMA k-steps over d for S^T and dP^T
+  constexpr int NDB = D / 32;  // 32-row blocks of d for dQ^T
+  constexpr int NL = 2 * TileLoadPlan<kDqWaves32, D>::NI;
+  __shared__ __attribute__((aligned(1024))) KvLds<D> s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int qt = a.rows.tasks[rank];
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t bhL = (int64_t)bh * L;
+  const uint16_t* Kg = (const uint16_t*)a.k + in_off;
+  const uint16_t* Vg = (const uint16_t*)a.v + in_off;
+  const int q_row = qt * BM + wave * 32 + l32;
+
+  // Q, dO of this lane's row as B operands (k-step kk: d = 16kk + 8hi ..),
+  // D = <dO, O> and the row's lse
+  bf16x8_t Qr[NKK], dOr[NKK];
+  float dpart = 0.f;
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const uint16_t* Qg = (const uint16_t*)a.q + in_off;
+    const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
+    const uint16_t* Og = (const uint16_t*)a.o + in_off;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int64_t off = q_row * a.isl + kk * 16 + 8 * hi;
+      Qr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
+      dOr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(dOg + off) : zero);
+      const bf16x8_t Or = as_bf16x8(q_row < L ? *(const u32x4_t*)(Og + off) : zero);
+      dpart = bf16_dot8(dOr[kk], Or, dpart);
+    }
+  }
+  const float lse_l2 = q_row < L ? a.lse[bhL + q_row] * kLog2e : 0.f;
+  wait_vmcnt<0>();
+  const float delta = dpart + wave_xor32(dpart);
+
+  const TileLoadPlan<kDqWaves32, D> plan(a.isl, wave, lane, swz_q32<D>);
+  auto prefetch = [&](int b, const Entry& x, int kti) {
+    issue_pair_loads<kDqWaves32, D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.rows.bits, x.pidx, lane);
+  };
+  const int e0 = a.rows.qt_off[qt], e1 = a.rows.qt_off[qt + 1];
+  int e = e0, kt = 0;
+  Entry en = {0, 0, -1, 0};
+  if (e < e1) {
+    en = a.rows.entries[e];
+    kt = en.kt0;
+    prefetch(0, en, kt);
+  }
+
+  f32x16_t dQacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dQacc[db][r] = 0.f;
+  const float sl2 = a.scale_log2;
+
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * D + (((2 * kk + hi) ^ swz_q32<D>(l32)) << 3);
+  const int g = lane >> 4, j = lane & 15;
+  const int vrow0 = 4 * hi + (j >> 2);
+  const int vd0 = 16 * (g & 1) + 4 * (j & 3);
+  int voff[2][NDB];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow0 + 8 * h8;
+      voff[h8][db] = row * D + (((4 * db + (vd0 >> 3)) ^ swz_q32<D>(row)) << 3) + (vd0 & 7);
+    }
+
+  int buf = 0;
+  while (e < e1) {
+    int e_n = e, kt_n = kt + 1;
+    Entry en_n = en;
+    if (kt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = a.rows.entries[e_n];
+        kt_n = en_n.kt0;
+      }
+    }
+    if (e_n < e1) {
+      prefetch(buf ^ 1, en_n, kt_n);
+      if (en_n.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
+      else wait_vmcnt<NL>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
+    const uint16_t* Kt = s.t[buf][0];
+    const uint16_t* Vt = s.t[buf][1];
+
+#pragma unroll 1
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query)
+      f32x16_t S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int off = kb * 32 * D + koff[kk];
+        const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
+        const bf16x8_t vop = as_bf16x8(*(const u32x4_t*)(Vt + off));
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, dOr[kk], dP, 0, 0, 0);
+      }
+      // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
+      bf16x8_t DS[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const int r = 8 * st + t;
+          const int key0 = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok0 = (bits >> key0) & 1ull, ok1 = (bits >> (key0 + 1)) & 1ull;
+          const float p0 = fast_exp2(__builtin_fmaf(S[r], sl2, -lse_l2));
+          const float p1 = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -lse_l2));
+          f32x2_t ds;
+          ds.x = ok0 ? p0 * (dP[r] - delta) : 0.f;
+          ds.y = ok1 ? p1 * (dP[r + 1] - delta) : 0.f;
+          const bf16x2_t d2 = __builtin_convertvector(ds, bf16x2_t);
+          DS[st][t] = d2.x;
+          DS[st][t + 1] = d2.y;
+        }
+      // dQ^T += K^T dS^T (rows = d, columns = queries)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int off_a = (kb * 32 + 16 * st) * D + voff[0][db];
+          const int off_b = (kb * 32 + 16 * st) * D + voff[1][db];
+          const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + off_a));
+          const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + off_b));
+          const bf16x8_t top = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dQacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top, DS[st], dQacc[db], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    e = e_n;
+    kt = kt_n;
+    en = en_n;
+    buf ^= 1;
+  }
+
+  if (q_row < L) {
+    const float c = a.scale;
+    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = db * 32 + 8 * gq + 4 * hi;
+        f32x4_t v;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = dQacc[db][4 * gq + jj] * c;
+        if constexpr (OUT_F32) *(f32x4_t*)((float*)a.dq + out_off + d0) = v;
+        else *(bf16x4_t*)((__bf16*)a.dq + out_off + d0) = __builtin_convertvector(v, bf16x4_t);
+      }
+    if (hi == 0) a.delta[bhL + q_row] = delta;
+  }
+}
+
 // ---- dK, dV -------------------------------------------------------------------
 
 template <int D, bool OUT_F32>
@@ -313,7 +497,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   // key bitmasks of a partial tile
   auto prefetch = [&](int b, const Entry& x, int qti) {
     const int row0 = qti * BN;
-    issue_pair_loads<D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
+    issue_pair_loads<kBwdWaves, D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
     if (wave == 1) {
       const int nrec = min(L - row0, BN) * 4;
       lds_dma_4(lds_addr(s.rowv[b][0]), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
@@ -488,8 +672,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 template <int D, bool OUT_F32>
 static void launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const dim3 block(64 * kBwdWaves);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_row_tasks) * a.B * a.H)), block, 0,
-                     stream, a);
+  hipLaunchKernelGGL((attn_bwd_dq32_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_row_tasks) * a.B * a.H)),
+                     dim3(64 * kDqWaves32), 0, stream, a);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_col_tasks) * a.B * a.H)), block, 0,
                      stream, a);
 }

@@ -81,18 +81,22 @@ constexpr float kLazyRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2
 constexpr int kWavesQ16 = 8;
 constexpr int kWavesQ32 = 4;
 
-template <int D>
+// Key-tile buffers of the bf16 kernels: NT = 4 tensors (K, tK, V, tV) for the
+// JVP, NT = 2 (K, V) for the primal forward, whose smaller footprint lets two
+// workgroups share a CU.
+template <int D, int NT>
 struct Bf16Lds {
   static constexpr int TILE = BN * D;  // elements per tensor tile
-  uint16_t t[2][4][TILE];              // [buffer][K, tK, V, tV]
+  uint16_t t[2][NT][TILE];             // [buffer][tensor]
   uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
+  // LDS slot of tensor t in {0: K, 1: tK, 2: V, 3: tV}
+  static constexpr __device__ int slot(int t) { return NT == 4 ? t : t / 2; }
 };
-
 // Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
 // when TANG, into one LDS buffer.  Returns immediately; completion is tracked
 // by vmcnt.  The buffer resource ends at row L, so rows past the end read as
 // zero.
-template <int NW, int D, bool TANG>
+template <int NW, int D, bool TANG, int NT>
 __device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* const src[4], int64_t sl, int key0, int L,
                                                  int wave) {
@@ -103,7 +107,7 @@ __device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const 
     const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
 #pragma unroll
     for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-      lds_dma_16(lds_addr(dst[t] + (wave + NW * i) * 512), plan.voff[i], rs);
+      lds_dma_16(lds_addr(dst[Bf16Lds<D, NT>::slot(t)] + (wave + NW * i) * 512), plan.voff[i], rs);
   }
 }
 
@@ -116,7 +120,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   constexpr int NDB = D / 16;  // 16-row blocks of d for the value products
   constexpr int NL_ALL = TileLoadPlan<kWavesQ16, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
   constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
-  using Lds = Bf16Lds<D>;
+  using Lds = Bf16Lds<D, 4>;
   __shared__ __attribute__((aligned(1024))) Lds s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
@@ -152,9 +156,9 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   // DMA of key tile kti of entry x (tangent tiles only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
     if (JVP && (!VARIANTS || x.flags == kTileJvp))
-      issue_tile_loads<kWavesQ16, D, true>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ16, D, true, 4>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
     else
-      issue_tile_loads<kWavesQ16, D, false>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
   };
   // wait until at most the loads of x's tile (issued last) are in flight
@@ -437,7 +441,9 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
   constexpr int NL_ALL = TileLoadPlan<kWavesQ32, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
   constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
-  __shared__ __attribute__((aligned(1024))) Bf16Lds<D> s;
+  constexpr int NT = JVP ? 4 : 2;
+  using Lds = Bf16Lds<D, NT>;
+  __shared__ __attribute__((aligned(1024))) Lds s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
@@ -460,9 +466,9 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   auto prefetch = [&](int b, const Entry& x, int kti) {
     (void)x.flags;
     if (JVP)
-      issue_tile_loads<kWavesQ32, D, true>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ32, D, true, NT>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
     else
-      issue_tile_loads<kWavesQ32, D, false>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
   };
   auto wait_all_but = [&](const Entry& x) {
@@ -535,10 +541,10 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
     constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
     const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
-    const uint16_t* Kt = s.t[buf][0];
-    const uint16_t* tKt = s.t[buf][1];
-    const uint16_t* Vt = s.t[buf][2];
-    const uint16_t* tVt = s.t[buf][3];
+    const uint16_t* Kt = s.t[buf][Lds::slot(0)];
+    const uint16_t* tKt = s.t[buf][Lds::slot(1)];
+    const uint16_t* Vt = s.t[buf][Lds::slot(2)];
+    const uint16_t* tVt = s.t[buf][Lds::slot(3)];
 
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -895,7 +901,11 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
 template <bool JVP, bool VARIANTS>
 static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid, hipStream_t stream) {
   const dim3 b16(64 * kWavesQ16), b32(64 * kWavesQ32);
-  if (head_dim == 128) {
+  if (!JVP && head_dim == 128) {
+    // primal forward: 32-row waves, two workgroups per CU
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, true, false>), grid, b32, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, false, false>), grid, b32, 0, stream, a);
+  } else if (head_dim == 128) {
     if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, JVP, VARIANTS>), grid, b16, 0, stream, a);
     else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, JVP, VARIANTS>), grid, b16, 0, stream, a);
   } else {

@@ -213,10 +213,11 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
 
 /* Primal masked attention (Eq. 42): O = softmax(scale * Q K^T + M) V and lse,
  * the forward of the student's packed teacher-forcing attention (Sec. 3.1.1,
- * Eq. 8) on the same descriptor as the JVP.  Same shapes, strides, checks and
- * results for O and lse as attn_jvp_fwd (bit for bit: the same kernel code
- * without the tangent products); in_dtype must be AJ_BF16 (AJ_ENOTSUP
- * otherwise).  o is [B, H, L, D] out_dtype, lse [B, H, L] float32.
+ * Eq. 8) on the same descriptor as the JVP.  Same shapes, strides and checks
+ * as attn_jvp_fwd; O and lse equal attn_jvp_fwd's bit for bit at head_dim 64
+ * (the same kernel code without the tangent products) and to rounding at 128
+ * (32-row waves instead of the JVP's 16).  in_dtype must be AJ_BF16
+ * (AJ_ENOTSUP otherwise).  o is [B, H, L, D] out_dtype, lse [B, H, L] float32.
  * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
 int32_t attn_fwd(const aj_shape* shape, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
                  float scale, void* o, float* lse, void* stream);

@@ -1,8 +1,9 @@
 """HIP primal masked attention (attn_fwd) vs the fp64 oracle and vs the JVP.
 
-attn_fwd runs the JVP kernel's code without the tangent products, so its O
-and lse must equal attn_jvp_fwd's bit for bit; against the oracle's O and lse
-the usual bf16 tolerances apply.
+At head_dim 64 attn_fwd runs the JVP kernel's code without the tangent
+products, so its O and lse equal attn_jvp_fwd's bit for bit; at 128 it runs
+32-row waves (a different summation order) and agrees to rounding.  Against
+the oracle's O and lse the usual bf16 tolerances apply.
 """
 import numpy as np
 import pytest
@@ -21,6 +22,19 @@ NAMES = ("q", "k", "v", "tq", "tk", "tv")
 def _desc(w):
     return aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
                                        head_dim=w.head_dim, dtype=w.dtype)
+
+
+def _same_as_jvp(o, lse, o_j, lse_j, D):
+    if D == 64:
+        assert torch.equal(o, o_j) and torch.equal(lse, lse_j)
+    else:
+        # both round p~ to bf16 before summing l, each against its own running
+        # max: lse agrees to the bf16 rounding of l, O to a few bf16 units
+        do = (o.float() - o_j.float()).abs().max().item()
+        dl = (lse - lse_j).abs().max().item()
+        print(f"[cmp] d128 primal vs jvp: max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+        assert do <= 2e-2 * max(1.0, o_j.float().abs().max().item())
+        assert dl <= 4e-3
 
 
 def _check_primal(w, got, ref, label):
@@ -55,7 +69,7 @@ def test_reduced_every_element_and_equal_to_jvp(case):
     o, lse = aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc, out_dtype=odt)
     o_j, _, lse_j = aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, out_dtype=odt)
     torch.cuda.synchronize()
-    assert torch.equal(o, o_j) and torch.equal(lse, lse_j)
+    _same_as_jvp(o, lse, o_j, lse_j, D)
     x = as_float64(inputs)
     ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale)
     _check_primal(w, [to_np(o), to_np(lse)], [ref[0], ref[2]], "primal")
@@ -71,7 +85,7 @@ def test_full_size_sampled_rows_and_equal_to_jvp(wname):
     o, lse = aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc)
     o_j, _, lse_j = aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc)
     torch.cuda.synchronize()
-    assert torch.equal(o, o_j) and torch.equal(lse, lse_j)
+    _same_as_jvp(o, lse, o_j, lse_j, w.head_dim)
     rows = sample_rows(w)
     x = {n: t.to(torch.float64).numpy() for n, t in inputs.items()}
     ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale, rows=rows)
