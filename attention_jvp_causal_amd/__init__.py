@@ -43,13 +43,22 @@ class aj_mask_stats(ctypes.Structure):
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("num_q_tiles", ctypes.c_int32), ("num_k_tiles", ctypes.c_int32),
                 ("full_tiles", ctypes.c_int32), ("partial_tiles", ctypes.c_int32),
-                ("num_entries", ctypes.c_int32)]
+                ("num_entries", ctypes.c_int32), ("kv_len", ctypes.c_int32)]
 
 
 class aj_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("in_stride_b", ctypes.c_int64), ("in_stride_h", ctypes.c_int64), ("in_stride_l", ctypes.c_int64),
+                ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_l", ctypes.c_int64)]
+
+
+class aj_kv_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("kv_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32),
+                ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64), ("q_stride_l", ctypes.c_int64),
+                ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
                 ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_l", ctypes.c_int64)]
 
 
@@ -80,11 +89,14 @@ def lib() -> ctypes.CDLL:
     L.attn_jvp_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
     L.attn_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, pdesc, f32, P, P, P]
     L.attn_bwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P, P]
+    L.attn_fwd_kv.argtypes = [ctypes.POINTER(aj_kv_shape), P, P, P, pdesc, f32, P, P, P]
+    L.attn_jvp_mask_desc_from_rects_kv.argtypes = [i32, i32, P, i32, i32, i32, ctypes.POINTER(pdesc)]
     L.attn_jvp_mask_desc_col_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
                "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
                "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
-               "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits"):
+               "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits", "attn_fwd_kv",
+               "attn_jvp_mask_desc_from_rects_kv"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -121,6 +133,7 @@ class MaskDesc:
         self.dtype = dtype
         s = self.stats()
         self.seq_len = s["seq_len"]
+        self.kv_len = s["kv_len"]
         self.unmasked_pairs = s["unmasked_pairs"]
 
     @property
@@ -202,6 +215,20 @@ def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], 
     _check(lib().attn_jvp_mask_desc_from_rects(seq_len, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 4,
                                                head_dim, dt, ctypes.byref(out)),
            "attn_jvp_mask_desc_from_rects")
+    return MaskDesc(out.value, head_dim, dt)
+
+
+def attn_jvp_mask_desc_from_rects_kv(q_len: int, kv_len: int, rects: Sequence[Sequence[int]], head_dim: int = 128,
+                                     dtype="bf16") -> MaskDesc:
+    """Descriptor for a query chunk of q_len tokens over kv_len cached keys, from
+    disjoint half-open rectangles (q0, q1, k0, k1)."""
+    flat = [int(x) for r in rects for x in r]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    out = ctypes.c_void_p()
+    dt = _dtype_code(dtype)
+    _check(lib().attn_jvp_mask_desc_from_rects_kv(q_len, kv_len, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 4,
+                                                  head_dim, dt, ctypes.byref(out)),
+           "attn_jvp_mask_desc_from_rects_kv")
     return MaskDesc(out.value, head_dim, dt)
 
 
@@ -303,6 +330,55 @@ def attn_fwd(q, k, v, mask: MaskDesc, scale: Optional[float] = None, out_dtype=N
     return o, lse
 
 
+def attn_fwd_kv(q, k_cache, v_cache, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
+                out: Optional[Tuple] = None, stream=None):
+    """O, lse of a query chunk q [B, H, Lq, D] over the first ``mask.kv_len``
+    positions of the caches k_cache, v_cache [B, H, >= kv_len, D] (bf16, D
+    contiguous, own strides).  ``out`` may pass preallocated (o, lse)."""
+    import torch
+
+    if q.dim() != 4 or k_cache.dim() != 4 or q.stride(3) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the caches must be [B, H, L, D] with D contiguous")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if any(t.device != q.device for t in (k_cache, v_cache)) or q.device.type != "cuda":
+        raise ValueError("all tensors must be on the same GPU device")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype")
+    B, H, Lq, D = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[1] != H or k_cache.shape[3] != D:
+        raise ValueError("cache batch, heads and head_dim must match q")
+    kv_len = mask.kv_len
+    if k_cache.shape[2] < kv_len:
+        raise ValueError(f"cache holds {k_cache.shape[2]} positions, the mask needs {kv_len}")
+    in_dt = {torch.bfloat16: AJ_BF16, torch.float32: AJ_F32}.get(q.dtype)
+    if in_dt is None:
+        raise ValueError(f"unsupported input dtype {q.dtype}")
+    odt = q.dtype if out_dtype is None else out_dtype
+    out_dt = {torch.bfloat16: AJ_BF16, torch.float32: AJ_F32}.get(odt)
+    if out_dt is None:
+        raise ValueError(f"unsupported output dtype {odt}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        o = torch.empty((B, H, Lq, D), dtype=odt, device=q.device)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if o.shape != q.shape or o.dtype != odt or o.stride(3) != 1:
+            raise ValueError("preallocated o has the wrong shape, dtype or layout")
+        if lse.shape != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("preallocated lse must be a contiguous float32 [B, H, Lq] tensor")
+    sh = aj_kv_shape(B, H, Lq, kv_len, D, in_dt, out_dt, *q.stride()[:3], *k_cache.stride()[:3], *o.stride()[:3])
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_kv(ctypes.byref(sh), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), mask.handle,
+                               float(scale), o.data_ptr(), lse.data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_fwd_kv")
+    return o, lse
+
+
 def attn_bwd(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
              out: Optional[Tuple] = None, stream=None):
     """dq, dk, dv of masked attention for the cotangent ``dout`` (bf16 inputs).
@@ -336,5 +412,5 @@ __all__ = [
     "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
     "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
-    "attn_jvp_fwd", "attn_fwd", "attn_bwd", "LIB_PATH",
+    "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_fwd", "attn_fwd_kv", "attn_bwd", "LIB_PATH",
 ]

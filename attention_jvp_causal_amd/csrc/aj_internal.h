@@ -74,7 +74,8 @@ struct DeviceTables {
 }  // namespace aj
 
 struct aj_mask_desc {
-  int32_t seq_len = 0, head_dim = 0, dtype = 0;
+  int32_t seq_len = 0, head_dim = 0, dtype = 0;  // seq_len: query length
+  int32_t kv_len = 0;                            // key length (= seq_len unless built for a KV cache)
   int32_t tile_m = aj::kTileM, tile_n = aj::kTileN;
   int64_t pairs = 0;
   std::vector<int32_t> rects;       // the admissible rectangles {q0,q1,k0,k1}
@@ -86,9 +87,10 @@ struct aj_mask_desc {
 };
 
 namespace aj {
-// Builds the tile map from validated, disjoint rectangles {q0,q1,k0,k1};
-// tfree holds n_tfree token ranges {t0,t1} whose tangents are declared zero.
-int32_t build_from_rects(int32_t seq_len, const int32_t* rects, int32_t n, int32_t head_dim,
+// Builds the tile maps from disjoint rectangles {q0,q1,k0,k1} inside
+// [0, q_len) x [0, kv_len); tfree holds n_tfree token ranges {t0,t1} whose
+// tangents are declared zero (square masks only).
+int32_t build_from_rects(int32_t q_len, int32_t kv_len, const int32_t* rects, int32_t n, int32_t head_dim,
                          int32_t dtype, const int32_t* tfree, int32_t n_tfree, aj_mask_desc** out);
 // Expands a frame-level layout into disjoint rectangles.
 int32_t layout_rects(const aj_mask_spec* spec, int32_t seq_len, std::vector<int32_t>* rects);

@@ -19,9 +19,11 @@ struct FwdArgs {
   void* o;
   void* to;
   float* lse;
-  int64_t isb, ish, isl;  // input strides (elements)
+  int64_t isb, ish, isl;  // query (and tangent) strides (elements)
+  int64_t ksb, ksh, ksl;  // key / value strides (elements)
   int64_t osb, osh, osl;  // output strides (elements)
   int32_t B, H, L, n_tasks;
+  int32_t Lk;             // key length (= L except for the KV-cache forward)
   float scale;       // softmax scale c
   float scale_log2;  // c * log2(e)
   const int32_t* qt_off;

@@ -73,39 +73,53 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
   return AJ_OK;
 }
 
+// Sizes and strides of one call: the square entry points take them from
+// aj_shape (keys and values share the queries' strides and length), the
+// KV-cache forward from aj_kv_shape.
+struct Geometry {
+  int32_t B, H, Lq, Lk, D, in_dtype, out_dtype;
+  int64_t qs[3], ks[3], os[3];  // strides (elements) over b, h, l
+};
+
+Geometry from_shape(const aj_shape* s) {
+  Geometry g{s->batch, s->heads, s->seq_len, s->seq_len, s->head_dim, s->in_dtype, s->out_dtype,
+             {s->in_stride_b, s->in_stride_h, s->in_stride_l}, {s->in_stride_b, s->in_stride_h, s->in_stride_l},
+             {s->out_stride_b, s->out_stride_h, s->out_stride_l}};
+  return g;
+}
+
 // Checks the arguments shared by the forward entry points and fills the
 // common launch arguments (q, k, v, o, lse, strides, sizes, scale, tables).
 // ins = {q, k, v, ...}, outs = {o, [to,] lse}; every pointer non-null and
 // 16-byte aligned.
-int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void* const* outs, int n_out,
-                const aj_mask_desc* mask, float scale, aj::FwdArgs* a) {
-  if (!s || !mask) return AJ_EINVAL;
+int32_t prepare_geom(const Geometry& s, const void* const* ins, int n_in, const void* const* outs, int n_out,
+                     const aj_mask_desc* mask, float scale, aj::FwdArgs* a) {
+  if (!mask) return AJ_EINVAL;
   for (int i = 0; i < n_in; ++i)
     if (!ins[i] || !aligned16(ins[i])) return AJ_EINVAL;
   for (int i = 0; i < n_out; ++i)
     if (!outs[i] || !aligned16(outs[i])) return AJ_EINVAL;
-  if (s->batch < 1 || s->heads < 1 || s->seq_len < 1) return AJ_EINVAL;
+  if (s.B < 1 || s.H < 1 || s.Lq < 1 || s.Lk < 1) return AJ_EINVAL;
   if (!std::isfinite(scale) || !(scale > 0.f)) return AJ_EINVAL;
-  if (!aj::supported_head_dim(s->head_dim)) return AJ_ENOTSUP;
-  if (!aj::supported_dtype(s->in_dtype) || !aj::supported_dtype(s->out_dtype)) return AJ_ENOTSUP;
-  if (s->in_dtype == AJ_F32 && s->out_dtype != AJ_F32) return AJ_ENOTSUP;
-  const int64_t esz_in = s->in_dtype == AJ_F32 ? 4 : 2, esz_out = s->out_dtype == AJ_F32 ? 4 : 2;
+  if (!aj::supported_head_dim(s.D)) return AJ_ENOTSUP;
+  if (!aj::supported_dtype(s.in_dtype) || !aj::supported_dtype(s.out_dtype)) return AJ_ENOTSUP;
+  if (s.in_dtype == AJ_F32 && s.out_dtype != AJ_F32) return AJ_ENOTSUP;
+  const int64_t esz_in = s.in_dtype == AJ_F32 ? 4 : 2, esz_out = s.out_dtype == AJ_F32 ? 4 : 2;
   const int64_t vin = 16 / esz_in, vout = 16 / esz_out;  // elements per 16 bytes
-  const int64_t D = s->head_dim, L = s->seq_len;
+  const int64_t D = s.D;
   // strides: non-negative, 16-byte multiples, rows at least D apart
-  const int64_t is[3] = {s->in_stride_b, s->in_stride_h, s->in_stride_l};
-  const int64_t os[3] = {s->out_stride_b, s->out_stride_h, s->out_stride_l};
   for (int i = 0; i < 3; ++i) {
-    if (is[i] < 0 || is[i] % vin != 0 || os[i] < 0 || os[i] % vout != 0) return AJ_EINVAL;
+    if (s.qs[i] < 0 || s.qs[i] % vin != 0 || s.ks[i] < 0 || s.ks[i] % vin != 0) return AJ_EINVAL;
+    if (s.os[i] < 0 || s.os[i] % vout != 0) return AJ_EINVAL;
   }
-  // input rows are read as whole rows through a 32-bit buffer range per key
+  // key rows are read as whole rows through a 32-bit buffer range per key
   // tile: distinct rows, and 64 rows' bytes must fit in 31 bits
-  if (is[2] < D || is[2] * esz_in * aj::kTileN >= (int64_t(1) << 31)) return AJ_EINVAL;
+  if (s.qs[2] < D || s.ks[2] < D || s.ks[2] * esz_in * aj::kTileN >= (int64_t(1) << 31)) return AJ_EINVAL;
   // outputs must not overlap themselves: sorted by stride, every stride must
   // clear the extent of the axes below it (rows are D elements long).  Inputs
   // are only read and may alias (a zero stride broadcasts).
   {
-    int64_t st3[3][2] = {{os[0], s->batch}, {os[1], s->heads}, {os[2], L}};
+    int64_t st3[3][2] = {{s.os[0], s.B}, {s.os[1], s.H}, {s.os[2], s.Lq}};
     for (int i = 0; i < 3; ++i)
       for (int j = i + 1; j < 3; ++j)
         if (st3[j][0] < st3[i][0]) std::swap(st3[i], st3[j]);
@@ -116,9 +130,9 @@ int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void*
       span = st3[i][0] * st3[i][1];
     }
   }
-  if (mask->seq_len != s->seq_len || mask->head_dim != s->head_dim || mask->dtype != s->in_dtype)
+  if (mask->seq_len != s.Lq || mask->kv_len != s.Lk || mask->head_dim != s.D || mask->dtype != s.in_dtype)
     return AJ_EMASK;
-  const int64_t BHL = int64_t(s->batch) * s->heads * L;
+  const int64_t BHL = int64_t(s.B) * s.H * std::max(s.Lq, s.Lk);
   if (BHL > (int64_t(1) << 40)) return AJ_EINVAL;
 
   const DeviceTables* t = nullptr;
@@ -130,14 +144,21 @@ int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void*
   r.q = ins[0]; r.k = ins[1]; r.v = ins[2];
   r.o = const_cast<void*>(outs[0]);
   r.lse = static_cast<float*>(const_cast<void*>(outs[n_out - 1]));
-  r.isb = s->in_stride_b; r.ish = s->in_stride_h; r.isl = s->in_stride_l;
-  r.osb = s->out_stride_b; r.osh = s->out_stride_h; r.osl = s->out_stride_l;
-  r.B = s->batch; r.H = s->heads; r.L = s->seq_len;
+  r.isb = s.qs[0]; r.ish = s.qs[1]; r.isl = s.qs[2];
+  r.ksb = s.ks[0]; r.ksh = s.ks[1]; r.ksl = s.ks[2];
+  r.osb = s.os[0]; r.osh = s.os[1]; r.osl = s.os[2];
+  r.B = s.B; r.H = s.H; r.L = s.Lq; r.Lk = s.Lk;
   r.n_tasks = mask->rows.n_qt;
   r.scale = scale;
   r.scale_log2 = float(double(scale) * 1.4426950408889634074);
   r.qt_off = t->rows.qt_off; r.entries = t->rows.entries; r.tasks = t->rows.tasks; r.bits = t->rows.bits;
   return AJ_OK;
+}
+
+int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void* const* outs, int n_out,
+                const aj_mask_desc* mask, float scale, aj::FwdArgs* a) {
+  if (!s) return AJ_EINVAL;
+  return prepare_geom(from_shape(s), ins, n_in, outs, n_out, mask, scale, a);
 }
 
 }  // namespace
@@ -168,8 +189,8 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
     std::vector<int32_t> rects;
     const int32_t st = aj::layout_rects(spec, seq_len, &rects);
     if (st != AJ_OK) return st;
-    return aj::build_from_rects(seq_len, rects.data(), int32_t(rects.size() / 4), head_dim, dtype, nullptr, 0,
-                                out);
+    return aj::build_from_rects(seq_len, seq_len, rects.data(), int32_t(rects.size() / 4), head_dim, dtype,
+                                nullptr, 0, out);
   } catch (const std::bad_alloc&) {
     return AJ_ENOMEM;
   } catch (...) {
@@ -179,7 +200,12 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
 
 int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
                                       int32_t head_dim, int32_t dtype, aj_mask_desc** out) {
-  return aj::build_from_rects(seq_len, rects, n_rects, head_dim, dtype, nullptr, 0, out);
+  return aj::build_from_rects(seq_len, seq_len, rects, n_rects, head_dim, dtype, nullptr, 0, out);
+}
+
+int32_t attn_jvp_mask_desc_from_rects_kv(int32_t q_len, int32_t kv_len, const int32_t* rects, int32_t n_rects,
+                                         int32_t head_dim, int32_t dtype, aj_mask_desc** out) {
+  return aj::build_from_rects(q_len, kv_len, rects, n_rects, head_dim, dtype, nullptr, 0, out);
 }
 
 int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t* ranges, int32_t n_ranges,
@@ -188,8 +214,8 @@ int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t*
   *out = nullptr;
   if (!base) return AJ_EINVAL;
   try {
-    return aj::build_from_rects(base->seq_len, base->rects.data(), int32_t(base->rects.size() / 4), base->head_dim,
-                                base->dtype, ranges, n_ranges, out);
+    return aj::build_from_rects(base->seq_len, base->kv_len, base->rects.data(), int32_t(base->rects.size() / 4),
+                                base->head_dim, base->dtype, ranges, n_ranges, out);
   } catch (const std::bad_alloc&) {
     return AJ_ENOMEM;
   } catch (...) {
@@ -214,6 +240,7 @@ int32_t attn_jvp_mask_desc_stats(const aj_mask_desc* d, aj_mask_stats* s) {
   s->full_tiles = d->rows.full_tiles;
   s->partial_tiles = d->rows.partial_tiles;
   s->num_entries = int32_t(d->rows.entries.size());
+  s->kv_len = d->kv_len;
   return AJ_OK;
 }
 
@@ -257,7 +284,7 @@ int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* d, int32_t qt, int32_t k
 int32_t attn_jvp_mask_desc_col_bits(const aj_mask_desc* d, int32_t k_tile, int32_t q_tile, int32_t key_row,
                                     uint64_t* bits) {
   if (!d) return AJ_EINVAL;
-  return map_bits(d->cols, d->seq_len, k_tile, q_tile, key_row, bits);
+  return map_bits(d->cols, d->kv_len, k_tile, q_tile, key_row, bits);
 }
 
 void attn_jvp_mask_desc_free(aj_mask_desc* d) {
@@ -310,6 +337,7 @@ int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v,
   if (st != AJ_OK) return st;
   if (!lse || !aligned16(lse)) return AJ_EINVAL;
   if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
+  if (mask->kv_len != mask->seq_len) return AJ_EMASK;
   const DeviceTables* t = nullptr;
   st = device_tables(mask, &t);
   if (st != AJ_OK) return st;
@@ -327,6 +355,24 @@ int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v,
   a.rows = t->rows;
   a.cols = t->cols;
   return aj::launch_bwd(a, s->out_dtype, s->head_dim, static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_fwd_kv(const aj_kv_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
+                    float scale, void* o, float* lse, void* stream) {
+  if (!s) return AJ_EINVAL;
+  const Geometry g{s->batch, s->heads, s->q_len, s->kv_len, s->head_dim, s->in_dtype, s->out_dtype,
+                   {s->q_stride_b, s->q_stride_h, s->q_stride_l}, {s->kv_stride_b, s->kv_stride_h, s->kv_stride_l},
+                   {s->out_stride_b, s->out_stride_h, s->out_stride_l}};
+  const void* ins[3] = {q, k, v};
+  const void* outs[2] = {o, lse};
+  aj::FwdArgs a;
+  int32_t st = prepare_geom(g, ins, 3, outs, 2, mask, scale, &a);
+  if (st != AJ_OK) return st;
+  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
+  a.tq = a.tk = a.tv = nullptr;
+  a.to = nullptr;
+  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, false, false,
+                        static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -130,10 +130,11 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   const int qt = a.tasks[rank];
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t kv_off = bb * a.ksb + hh * a.ksh;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
   const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, JVP ? (const uint16_t*)a.tk + in_off : nullptr,
-                                  (const uint16_t*)a.v + in_off, JVP ? (const uint16_t*)a.tv + in_off : nullptr};
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
+                                  (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
   const int q_row = qt * BM + wave * 16 + j16;
 
   // Q and tQ of this lane's query row, as B operands: k-step ks holds
@@ -152,13 +153,13 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   // load inside the tile loop.
   wait_vmcnt<0>();
 
-  const TileLoadPlan<kWavesQ16, D> plan(a.isl, wave, lane, swz_q16<D>);
+  const TileLoadPlan<kWavesQ16, D> plan(a.ksl, wave, lane, swz_q16<D>);
   // DMA of key tile kti of entry x (tangent tiles only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
     if (JVP && (!VARIANTS || x.flags == kTileJvp))
-      issue_tile_loads<kWavesQ16, D, true, 4>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ16, D, true, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
-      issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
   };
   // wait until at most the loads of x's tile (issued last) are in flight
@@ -452,13 +453,14 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   const int qt = a.tasks[rank];
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t kv_off = bb * a.ksb + hh * a.ksh;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
   const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + in_off, JVP ? (const uint16_t*)a.tk + in_off : nullptr,
-                                  (const uint16_t*)a.v + in_off, JVP ? (const uint16_t*)a.tv + in_off : nullptr};
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
+                                  (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
   const int q_row = qt * BM + wave * 32 + l32;
 
-  const TileLoadPlan<kWavesQ32, D> plan(a.isl, wave, lane, swz_q32<D>);
+  const TileLoadPlan<kWavesQ32, D> plan(a.ksl, wave, lane, swz_q32<D>);
   // At d = 64 the tangent-free variants are not built (three copies of the
   // tile code do not fit the register budget of two workgroups per CU): every
   // tile runs the general code, which is exact when the declared tangents are
@@ -466,9 +468,9 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   auto prefetch = [&](int b, const Entry& x, int kti) {
     (void)x.flags;
     if (JVP)
-      issue_tile_loads<kWavesQ32, D, true, NT>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ32, D, true, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
-      issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.isl, kti * BN, L, wave);
+      issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
   };
   auto wait_all_but = [&](const Entry& x) {
@@ -768,11 +770,12 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const float* __restrict__ Qg = (const float*)a.q + in_off;
-  const float* __restrict__ Kg = (const float*)a.k + in_off;
-  const float* __restrict__ Vg = (const float*)a.v + in_off;
+  const int64_t kv_off = bb * a.ksb + hh * a.ksh;
+  const float* __restrict__ Kg = (const float*)a.k + kv_off;
+  const float* __restrict__ Vg = (const float*)a.v + kv_off;
   const float* __restrict__ tQg = (const float*)a.tq + in_off;
-  const float* __restrict__ tKg = (const float*)a.tk + in_off;
-  const float* __restrict__ tVg = (const float*)a.tv + in_off;
+  const float* __restrict__ tKg = (const float*)a.tk + kv_off;
+  const float* __restrict__ tVg = (const float*)a.tv + kv_off;
   const int q_row = qt * BM + wave * 32 + l32;
 
   float Qr[NKK], tQr[NKK];
@@ -797,10 +800,10 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
     const uint64_t bits = en.pidx >= 0 ? a.bits[(int64_t)en.pidx * BM + wave * 32 + l32] : ~0ull;
     for (int kt = en.kt0; kt < en.kt1; ++kt) {
       __syncthreads();
-      stage_one_f32<D>(s.k, Kg, a.isl, kt * BN, L, tid);
-      stage_one_f32<D>(s.tk, tKg, a.isl, kt * BN, L, tid);
-      stage_one_f32<D>(s.v, Vg, a.isl, kt * BN, L, tid);
-      stage_one_f32<D>(s.tv, tVg, a.isl, kt * BN, L, tid);
+      stage_one_f32<D>(s.k, Kg, a.ksl, kt * BN, a.Lk, tid);
+      stage_one_f32<D>(s.tk, tKg, a.ksl, kt * BN, a.Lk, tid);
+      stage_one_f32<D>(s.v, Vg, a.ksl, kt * BN, a.Lk, tid);
+      stage_one_f32<D>(s.tv, tVg, a.ksl, kt * BN, a.Lk, tid);
       __syncthreads();
 
 #pragma unroll 1

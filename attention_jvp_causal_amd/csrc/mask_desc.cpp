@@ -19,10 +19,10 @@ namespace aj {
 
 namespace {
 
-int32_t validate_rects(int32_t L, const int32_t* r, int32_t n) {
+int32_t validate_rects(int32_t Lq, int32_t Lk, const int32_t* r, int32_t n) {
   for (int32_t i = 0; i < n; ++i) {
     const int32_t q0 = r[4 * i], q1 = r[4 * i + 1], k0 = r[4 * i + 2], k1 = r[4 * i + 3];
-    if (q0 < 0 || q0 >= q1 || q1 > L || k0 < 0 || k0 >= k1 || k1 > L) return AJ_EMASK;
+    if (q0 < 0 || q0 >= q1 || q1 > Lq || k0 < 0 || k0 >= k1 || k1 > Lk) return AJ_EMASK;
   }
   // pairwise disjointness: sort by q0, compare only rectangles whose query
   // ranges overlap
@@ -119,16 +119,18 @@ int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out
 }
 
 // Tile map of rectangles r (owner axis first: {o0, o1, v0, v1}) with owner
-// tiles of kTileM and visited tiles of kTileN.  tfree (merged ranges) marks
-// tangent-free tokens; both axes index the same sequence.
-static void build_map(int32_t L, const int32_t* r, int32_t n, const std::vector<int32_t>& tfree, TileMap* m) {
+// tiles of kTileM over [0, Lo) and visited tiles of kTileN over [0, Lv).
+// tfree (merged ranges) marks tangent-free tokens (square masks: both axes
+// index the same sequence).
+static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const std::vector<int32_t>& tfree,
+                      TileMap* m) {
   const int32_t BM = kTileM, BN = kTileN;
-  m->n_qt = (L + BM - 1) / BM;
-  m->n_kt = (L + BN - 1) / BN;
+  m->n_qt = (Lo + BM - 1) / BM;
+  m->n_kt = (Lv + BN - 1) / BN;
   // tangent-free owner and visited tiles: every token of the tile inside
-  // [0, L) is declared tangent-free
-  auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(L, qt * BM + BM)); };
-  auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(L, kt * BN + BN)); };
+  // the sequence is declared tangent-free
+  auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(Lo, qt * BM + BM)); };
+  auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(Lv, kt * BN + BN)); };
   auto variant = [&](bool qf, int32_t kt) {
     return k_free(kt) ? (qf ? kTileAllFree : kTileKeysFree) : kTileJvp;
   };
@@ -145,7 +147,7 @@ static void build_map(int32_t L, const int32_t* r, int32_t n, const std::vector<
   for (int32_t qt = 0; qt < m->n_qt; ++qt) {
     m->qt_off[qt] = int32_t(m->entries.size());
     const bool qf = q_free(qt);
-    const int32_t a = qt * BM, b = std::min(L, a + BM);
+    const int32_t a = qt * BM, b = std::min(Lo, a + BM);
     const int64_t full_count = int64_t(b - a) * BN;  // allowed pairs in a full tile
     // allowed-pair count per visited tile: runs of interior tiles go into a
     // difference map, the (at most two) boundary tiles of each rectangle
@@ -186,7 +188,7 @@ static void build_map(int32_t L, const int32_t* r, int32_t n, const std::vector<
       // is exactly one tile wide
       const int32_t e1 = s1;
       if (cnt == 0) continue;
-      const bool in_range = int64_t(e1) * BN <= L;
+      const bool in_range = int64_t(e1) * BN <= Lv;
       if (cnt == full_count && in_range) {
         for (int32_t kt = s0; kt < e1; ++kt) {
           const int32_t fl = variant(qf, kt);
@@ -234,28 +236,30 @@ static void build_map(int32_t L, const int32_t* r, int32_t n, const std::vector<
   });
 }
 
-int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,
+int32_t build_from_rects(int32_t Lq, int32_t Lk, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,
                          const int32_t* tf, int32_t n_tf, aj_mask_desc** out) {
   if (!out) return AJ_EINVAL;
   *out = nullptr;
-  if (L < 1 || n < 0 || (n > 0 && !r) || n_tf < 0 || (n_tf > 0 && !tf)) return AJ_EINVAL;
+  if (Lq < 1 || Lk < 1 || n < 0 || (n > 0 && !r) || n_tf < 0 || (n_tf > 0 && !tf)) return AJ_EINVAL;
+  if (n_tf > 0 && Lq != Lk) return AJ_EINVAL;
   if (!supported_head_dim(head_dim) || !supported_dtype(dtype)) return AJ_ENOTSUP;
-  int32_t st = validate_rects(L, r, n);
+  int32_t st = validate_rects(Lq, Lk, r, n);
   if (st != AJ_OK) return st;
   std::vector<int32_t> tfree;
-  st = merge_ranges(L, tf, n_tf, &tfree);
+  st = merge_ranges(Lq, tf, n_tf, &tfree);
   if (st != AJ_OK) return st;
 
   aj_mask_desc* d = new (std::nothrow) aj_mask_desc();
   if (!d) return AJ_ENOMEM;
   try {
-    d->seq_len = L;
+    d->seq_len = Lq;
+    d->kv_len = Lk;
     d->head_dim = head_dim;
     d->dtype = dtype;
     d->rects.assign(r, r + 4 * size_t(n));
     d->tfree = tfree;
     for (int32_t i = 0; i < n; ++i) d->pairs += int64_t(r[4 * i + 1] - r[4 * i]) * (r[4 * i + 3] - r[4 * i + 2]);
-    build_map(L, r, n, tfree, &d->rows);
+    build_map(Lq, Lk, r, n, tfree, &d->rows);
     // the transposed mask: key tiles own runs of query tiles (no variants)
     std::vector<int32_t> tr(4 * size_t(n));
     for (int32_t i = 0; i < n; ++i) {
@@ -264,7 +268,7 @@ int32_t build_from_rects(int32_t L, const int32_t* r, int32_t n, int32_t head_di
       tr[4 * i + 2] = r[4 * i];
       tr[4 * i + 3] = r[4 * i + 1];
     }
-    build_map(L, tr.data(), n, std::vector<int32_t>(), &d->cols);
+    build_map(Lk, Lq, tr.data(), n, std::vector<int32_t>(), &d->cols);
   } catch (const std::bad_alloc&) {
     delete d;
     return AJ_ENOMEM;

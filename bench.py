@@ -16,7 +16,10 @@ Other measurements of the same kernels (one JSON line each, same schema):
   --op fwd         primal masked attention (O, lse): 4d FLOP per pair;
   --op bwd         its gradients (dq, dk, dv from o, lse, dO): 10d FLOP per pair
                    by the usual count of five products (the kernels execute 14d:
-                   the scores and dP are formed once per kernel).
+                   the scores and dP are formed once per kernel);
+  --op kv          rollout step with a KV cache: the workload's last chunk of
+                   queries over the whole sequence's keys held as a cache
+                   (block-causal workloads): 4d FLOP per pair.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
@@ -40,6 +43,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak, 1 GPU"
 METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_BWD = "masked attention backward TFLOP/s (unmasked FLOPs, 10d per pair) and % of bf16 MFMA peak, 1 GPU"
+METRIC_KV = "KV-cache chunk attention TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n) for n in ("aj_device.h", "attn_jvp_fwd.hip")]
 
 
@@ -170,8 +174,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=None, help="workload name (default: the c3-3 Wan2.1-1.3B shape)")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads timed for the oracle baseline (0 = skip)")
-    ap.add_argument("--op", default="jvp", choices=["jvp", "fwd", "bwd"],
-                    help="jvp: O, tO, lse (the metric); fwd: primal O, lse only; bwd: dq, dk, dv")
+    ap.add_argument("--op", default="jvp", choices=["jvp", "fwd", "bwd", "kv"],
+                    help="jvp: O, tO, lse (the metric); fwd: primal O, lse only; bwd: dq, dk, dv; "
+                         "kv: last chunk over a KV cache")
     ap.add_argument("--tangent-free", action="store_true",
                     help="declare the clean half of a teacher-forcing workload tangent-free")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -209,8 +214,15 @@ def main(argv=None):
         if not w.clean_tangent_zero:
             raise SystemExit(f"--tangent-free needs a workload whose clean half has zero tangents, not {w.name}")
         desc = aj.attn_jvp_mask_desc_tangent_free(desc, [(0, w.seq_len // 2)])
+    if args.op == "kv":
+        if w.mask_kind != "block_causal":
+            raise SystemExit("--op kv needs a block-causal workload")
+        chunk = w.frames_per_chunk * w.frame_tokens
+        q_len = w.seq_len - ((w.seq_len - 1) // chunk) * chunk  # the last (possibly ragged) chunk
+        desc = aj.attn_jvp_mask_desc_from_rects_kv(q_len, w.seq_len, [(0, q_len, 0, w.seq_len)],
+                                                   head_dim=w.head_dim, dtype=w.dtype)
     pairs = desc.unmasked_pairs * w.batch * w.heads
-    per_pair = {"jvp": 12.0, "fwd": 4.0, "bwd": 10.0}[args.op]
+    per_pair = {"jvp": 12.0, "fwd": 4.0, "bwd": 10.0, "kv": 4.0}[args.op]
     flop = per_pair * w.head_dim * pairs
     # FLOPs the kernels execute: fewer than the convention's on tangent-free
     # tiles; more for the gradients (14d)
@@ -237,8 +249,15 @@ def main(argv=None):
         grads = tuple(torch.empty((B, H, L, D), dtype=odt, device="cuda:0") for _ in range(3)) + (
             torch.empty((B, H, L), dtype=torch.float32, device="cuda:0"),)
 
+    if args.op == "kv":
+        q_chunk = dev["q"][:, :, w.seq_len - q_len:].contiguous()
+        o_kv = torch.empty_like(q_chunk, dtype=odt)
+        lse_kv = torch.empty((B, H, q_len), dtype=torch.float32, device="cuda:0")
+
     def step():
-        if args.op == "jvp":
+        if args.op == "kv":
+            aj.attn_fwd_kv(q_chunk, dev["k"], dev["v"], desc, scale=w.scale, out_dtype=out_dtype, out=(o_kv, lse_kv))
+        elif args.op == "jvp":
             aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
         elif args.op == "fwd":
             aj.attn_fwd(*args_[:3], desc, scale=w.scale, out_dtype=out_dtype, out=(outs[0], outs[2]))
@@ -275,9 +294,12 @@ def main(argv=None):
     achieved = exec_flop / (avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     traffic = measured_traffic(w.name)
-    n_in, n_out = {"jvp": (6, 2), "fwd": (3, 1), "bwd": (5, 3)}[args.op]
+    n_in, n_out = {"jvp": (6, 2), "fwd": (3, 1), "bwd": (5, 3), "kv": (2, 0)}[args.op]
     in_bytes = n_in * B * H * L * D * inputs["q"].element_size() + (B * H * L * 4 if args.op == "bwd" else 0)
     out_bytes = n_out * B * H * L * D * odt.itemsize + B * H * L * 4
+    if args.op == "kv":  # K, V of the cache; q and o of the chunk; lse
+        in_bytes += B * H * q_len * D * inputs["q"].element_size()
+        out_bytes = B * H * q_len * (D * odt.itemsize + 4)
     if args.op != "jvp" or args.tangent_free:
         traffic = None  # counters are recorded for the plain JVP only
 
@@ -285,7 +307,7 @@ def main(argv=None):
     if args.cpu_heads > 0 and args.op == "jvp":
         cpu = cpu_baseline(w, inputs, min(args.cpu_heads, w.heads))
 
-    metric = {"jvp": METRIC, "fwd": METRIC_FWD, "bwd": METRIC_BWD}[args.op]
+    metric = {"jvp": METRIC, "fwd": METRIC_FWD, "bwd": METRIC_BWD, "kv": METRIC_KV}[args.op]
     rec = {
         "metric": metric,
         "value": round(value, 2),
@@ -307,6 +329,7 @@ def main(argv=None):
             "unmasked_pairs": pairs,
             "flop_per_step": flop,
             "op": args.op,
+            "kv_cache": (f"last chunk of {q_len} queries over {L} cached keys" if args.op == "kv" else None),
             "tangent_free": ("clean half [0, L/2) declared tangent-free; value counts 12d per pair, "
                              "roofline the executed 12d / 8d / 4d per pair by tile class")
                             if args.tangent_free else None,
@@ -323,7 +346,7 @@ def main(argv=None):
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel": (kernel_name(w.dtype, D, odt == torch.float32, args.op == "jvp", args.tangent_free)
-                       if args.op != "bwd" else "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel"),
+                       if args.op != "bwd" else "attn_bwd_dq32_kernel + attn_bwd_dkdv_kernel"),
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,

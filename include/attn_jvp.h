@@ -91,6 +91,7 @@ typedef struct {
   int32_t full_tiles;       /* tiles with every (query < L, key) pair allowed */
   int32_t partial_tiles;    /* tiles with some, not all, pairs allowed */
   int32_t num_entries;      /* span entries over all query tiles */
+  int32_t kv_len;           /* key length (= seq_len except for KV-cache descriptors) */
 } aj_mask_stats;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -116,6 +117,16 @@ int32_t attn_jvp_mask_desc_build(const aj_mask_spec* spec, int32_t seq_len, int3
  * overlap or out-of-range rectangle gives AJ_EMASK. */
 int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int32_t n_rects,
                                       int32_t head_dim, int32_t dtype, aj_mask_desc** out);
+
+/* Build a descriptor whose queries and keys are different sequences: the
+ * current chunk of an autoregressive rollout (q_len tokens) attending keys
+ * held in a KV cache (kv_len tokens; Sec. 3.2.1 "KV Cache": a readonly
+ * forward exposes only the committed prefix the current chunk needs).  rects
+ * holds n_rects * 4 int32 {q0, q1, k0, k1}, half-open, disjoint, inside
+ * [0, q_len) x [0, kv_len).  Only attn_fwd_kv accepts such a descriptor when
+ * kv_len != q_len.  Host-only.  Errors as for attn_jvp_mask_desc_from_rects. */
+int32_t attn_jvp_mask_desc_from_rects_kv(int32_t q_len, int32_t kv_len, const int32_t* rects, int32_t n_rects,
+                                         int32_t head_dim, int32_t dtype, aj_mask_desc** out);
 
 /* Derive a descriptor that also knows which tokens carry no tangent.
  * In teacher-forcing sCM / MeanFlow the JVP runs through the packed
@@ -221,6 +232,27 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
  * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
 int32_t attn_fwd(const aj_shape* shape, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
                  float scale, void* o, float* lse, void* stream);
+
+/* Shapes and strides of a KV-cache forward.  Queries [B, H, q_len, D] with
+ * q strides; keys and values [B, H, kv_len, D] inside a cache buffer with
+ * their own strides (the post-all-to-all [B, H/P, L, C] cache layout of
+ * Sec. 3.2.1, of which the first kv_len positions are used); the output
+ * [B, H, q_len, D] with out strides.  Strides in elements, D contiguous. */
+typedef struct {
+  int32_t batch, heads, q_len, kv_len, head_dim, in_dtype, out_dtype;
+  int64_t q_stride_b, q_stride_h, q_stride_l;
+  int64_t kv_stride_b, kv_stride_h, kv_stride_l;
+  int64_t out_stride_b, out_stride_h, out_stride_l;
+} aj_kv_shape;
+
+/* Primal masked attention of a query chunk over a KV cache (readonly mode of
+ * Sec. 3.2.1: the chunk being generated attends the committed prefix, and
+ * itself once its keys sit in the cache slots after the prefix).  Same
+ * operation, kernels, checks and errors as attn_fwd with the key length and
+ * strides taken from the shape; the descriptor must have been built for
+ * (q_len, kv_len).  lse is [B, H, q_len] float32.  in_dtype must be AJ_BF16. */
+int32_t attn_fwd_kv(const aj_kv_shape* shape, const void* q, const void* k, const void* v,
+                    const aj_mask_desc* mask, float scale, void* o, float* lse, void* stream);
 
 /* Gradients of masked attention for a cotangent dout: dq, dk, dv of
  * O = softmax(scale * Q K^T + M) V, the backward of attn_fwd on the same

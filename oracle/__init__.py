@@ -24,11 +24,11 @@ autodiff of a dense masked attention and of PyTorch's SDPA, by the adjoint
 identity with the (separately pinned) JVP, by central finite differences and by
 their sum rules.  Every function here is pinned; none is "parity unpinned".
 """
-from .masks import MaskLayout, RectMask, allowed, key_ranges, dense_mask, unmasked_pairs
+from .masks import MaskLayout, RectMask, allowed, chunk_over_cache, key_ranges, dense_mask, unmasked_pairs
 from .attention_jvp import attn_jvp_ref, unmasked_pairs_rows
 from .attention_vjp import attn_vjp_ref, attn_vjp_sampled
 
 __all__ = [
-    "MaskLayout", "RectMask", "allowed", "key_ranges", "dense_mask", "unmasked_pairs",
+    "MaskLayout", "RectMask", "allowed", "chunk_over_cache", "key_ranges", "dense_mask", "unmasked_pairs",
     "attn_jvp_ref", "unmasked_pairs_rows", "attn_vjp_ref", "attn_vjp_sampled",
 ]

@@ -22,7 +22,7 @@ notes):
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import List, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -60,9 +60,26 @@ class MaskLayout:
 
 @dataclass(frozen=True)
 class RectMask:
-    """A mask given directly as admissible rectangles [q0,q1) x [k0,k1) (App. B)."""
+    """A mask given directly as admissible rectangles [q0,q1) x [k0,k1) (App. B).
+
+    seq_len is the number of query rows; kv_len the number of keys when the
+    keys are another sequence (a query chunk over a KV cache, Sec. 3.2.1
+    "KV Cache"), else the same as seq_len."""
     seq_len: int
     rects: Tuple[Tuple[int, int, int, int], ...]
+    kv_len: Optional[int] = None
+
+    @property
+    def key_len(self) -> int:
+        return self.seq_len if self.kv_len is None else self.kv_len
+
+
+def chunk_over_cache(chunk_len: int, prefix_len: int) -> RectMask:
+    """Readonly KV-cache attention of one chunk (Sec. 3.2.1 "KV Cache"): the
+    chunk's queries see the committed prefix and, with the chunk's own keys
+    placed after it, every key of the chunk (attention inside a chunk is full)."""
+    kv = prefix_len + chunk_len
+    return RectMask(chunk_len, ((0, chunk_len, 0, kv),), kv_len=kv)
 
 
 def allowed(mask, i: int, j: int) -> bool:
@@ -118,9 +135,10 @@ def key_ranges(mask, i: int) -> List[Tuple[int, int]]:
 
 
 def dense_mask(mask) -> np.ndarray:
-    """Boolean [L, L] matrix built from the element predicate (tiny L only)."""
+    """Boolean [L, Lk] matrix built from the element predicate (tiny L only)."""
     L = mask.seq_len
-    return np.array([[allowed(mask, i, j) for j in range(L)] for i in range(L)], dtype=bool)
+    Lk = mask.key_len if isinstance(mask, RectMask) else L
+    return np.array([[allowed(mask, i, j) for j in range(Lk)] for i in range(L)], dtype=bool)
 
 
 def unmasked_pairs(mask) -> int:

@@ -160,3 +160,51 @@ def test_column_map_is_the_transposed_mask(mask):
                 assert got == want, (kt, qt, r)
                 pairs += bin(got).count("1")
     assert pairs == unmasked_pairs(mask)
+
+
+@pytest.mark.parametrize("Lq,Lk,rects", [
+    (300, 1000, ((0, 300, 0, 1000),)),
+    (130, 70, ((0, 60, 0, 70), (60, 130, 5, 66))),
+    (200, 4680, ((0, 100, 0, 4000), (100, 200, 0, 4680))),
+])
+def test_kv_descriptor_maps(Lq, Lk, rects):
+    m = RectMask(Lq, rects, kv_len=Lk)
+    d = aj.attn_jvp_mask_desc_from_rects_kv(Lq, Lk, rects, head_dim=128, dtype="bf16")
+    st = d.stats()
+    assert st["seq_len"] == Lq and st["kv_len"] == Lk and st["unmasked_pairs"] == unmasked_pairs(m)
+    assert st["num_q_tiles"] == -(-Lq // 128) and st["num_k_tiles"] == -(-Lk // 64)
+    dm = dense_mask(m)
+    rng = np.random.default_rng(1)
+    for _ in range(40):
+        qt, kt = int(rng.integers(st["num_q_tiles"])), int(rng.integers(st["num_k_tiles"]))
+        for r in (0, 5, 127, int(rng.integers(128))):
+            i = qt * 128 + r
+            want = 0
+            if i < Lq:
+                for j in range(64):
+                    if kt * 64 + j < Lk and dm[i, kt * 64 + j]:
+                        want |= 1 << j
+            got = d.row_bits(qt, kt, r)
+            if d.tile_kind(qt, kt) == 2 and i < Lq:
+                assert want == (1 << 64) - 1
+            else:
+                assert got == want
+        kk, qq = int(rng.integers(-(-Lk // 128))), int(rng.integers(-(-Lq // 64)))
+        for r in (0, 77, 127):
+            key = kk * 128 + r
+            want = 0
+            if key < Lk:
+                for j in range(64):
+                    if qq * 64 + j < Lq and dm[qq * 64 + j, key]:
+                        want |= 1 << j
+            assert d.col_bits(kk, qq, r) == want
+
+
+def test_kv_descriptor_errors():
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_mask_desc_from_rects_kv(10, 20, [(0, 10, 0, 21)], head_dim=128, dtype="bf16")
+    assert e.value.status == aj.AJ_EMASK
+    d = aj.attn_jvp_mask_desc_from_rects_kv(10, 20, [(0, 10, 0, 20)], head_dim=128, dtype="bf16")
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_mask_desc_tangent_free(d, [(0, 5)])
+    assert e.value.status == aj.AJ_EINVAL
