@@ -21,9 +21,10 @@
 //   dP = dO V^T with K and V of the lane's key as B operands): one key per
 //   lane column, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly,
 //   dO^T and Q^T coming from transpose reads.
-// Both use 8 waves of 16 rows (v_mfma_f32_16x16x32_bf16, two waves per
-// SIMD), the direct buffer -> LDS DMA into a double buffer and the swizzled
-// tile layout of the forward kernels.  Masked pairs are removed by select
+// dQ runs 4 waves of 32 rows (v_mfma_f32_32x32x16_bf16, two workgroups per
+// CU), dK / dV 8 waves of 16 keys (v_mfma_f32_16x16x32_bf16, two waves per
+// SIMD); both use the direct buffer -> LDS DMA into a double buffer and the
+// swizzled tile layouts of the forward kernels.  Masked pairs are removed by select
 // (P = dS = 0), never by arithmetic on -inf.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -91,193 +92,6 @@ __device__ __forceinline__ float bf16_dot8(bf16x8_t x, bf16x8_t y, float acc) {
 }
 
 // ---- dQ (and D) ---------------------------------------------------------------
-
-template <int D, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves), amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int NKS = D / 32;  // MFMA k-steps over d for S^T and dP^T
-  constexpr int NDB = D / 16;  // 16-row blocks of d for dQ^T
-  constexpr int NL = 2 * TileLoadPlan<kBwdWaves, D>::NI;  // DMA per wave per tile
-  __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
-  const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
-  const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.rows.tasks[rank];
-  const int L = a.L;
-  const int64_t in_off = bb * a.isb + hh * a.ish;
-  const int64_t bhL = (int64_t)bh * L;
-  const uint16_t* Kg = (const uint16_t*)a.k + in_off;
-  const uint16_t* Vg = (const uint16_t*)a.v + in_off;
-  const int q_row = qt * BM + wave * 16 + j16;
-
-  // Q, dO of this lane's row as B operands (k-step ks: d = 32ks + 8g ..),
-  // D = <dO, O> and the row's lse
-  bf16x8_t Qr[NKS], dOr[NKS];
-  float dpart = 0.f;
-  {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    const uint16_t* Qg = (const uint16_t*)a.q + in_off;
-    const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
-    const uint16_t* Og = (const uint16_t*)a.o + in_off;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int64_t off = q_row * a.isl + ks * 32 + 8 * g;
-      Qr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
-      dOr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(dOg + off) : zero);
-      const bf16x8_t Or = as_bf16x8(q_row < L ? *(const u32x4_t*)(Og + off) : zero);
-      dpart = bf16_dot8(dOr[ks], Or, dpart);
-    }
-  }
-  const float lse_l2 = q_row < L ? a.lse[bhL + q_row] * kLog2e : 0.f;
-  wait_vmcnt<0>();
-  const float delta = row4_sum(dpart);
-
-  const TileLoadPlan<kBwdWaves, D> plan(a.isl, wave, lane, swz_q16<D>);
-  auto prefetch = [&](int b, const Entry& x, int kti) {
-    issue_pair_loads<kBwdWaves, D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.rows.bits, x.pidx, lane);
-  };
-  const int e0 = a.rows.qt_off[qt], e1 = a.rows.qt_off[qt + 1];
-  int e = e0, kt = 0;
-  Entry en = {0, 0, -1, 0};
-  if (e < e1) {
-    en = a.rows.entries[e];
-    kt = en.kt0;
-    prefetch(0, en, kt);
-  }
-
-  f32x4_t dQacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dQacc[db][r] = 0.f;
-  const float sl2 = a.scale_log2;
-
-  // LDS offsets as in the forward kernel: row operand of 16-key block kb,
-  // k-step ks at kb*16*D + koff[ks]; transpose-read operand of value k-step p,
-  // d block db at 32p*D + voff[h][db].
-  int koff[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
-  const int vrow = 4 * g + (j16 >> 2);
-  int voff[2][NDB];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int row = vrow + 16 * h;
-      const int chunk = 2 * db + ((j16 & 3) >> 1);
-      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
-    }
-
-  int buf = 0;
-  while (e < e1) {
-    int e_n = e, kt_n = kt + 1;
-    Entry en_n = en;
-    if (kt_n >= en.kt1) {
-      e_n = e + 1;
-      if (e_n < e1) {
-        en_n = a.rows.entries[e_n];
-        kt_n = en_n.kt0;
-      }
-    }
-    if (e_n < e1) {
-      prefetch(buf ^ 1, en_n, kt_n);
-      if (en_n.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
-      else wait_vmcnt<NL>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
-    const uint16_t* Kt = s.t[buf][0];
-    const uint16_t* Vt = s.t[buf][1];
-
-    // S^T = K Q^T and dP^T = V dO^T for the 64 keys of the tile
-    f32x4_t S[4], dP[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[kb][r] = dP[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8_t kop[4], vop[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int off = kb * 16 * D + koff[ks];
-        kop[kb] = as_bf16x8(*(const u32x4_t*)(Kt + off));
-        vop[kb] = as_bf16x8(*(const u32x4_t*)(Vt + off));
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], Qr[ks], S[kb], 0, 0, 0);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        dP[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[kb], dOr[ks], dP[kb], 0, 0, 0);
-    }
-    // lane holds keys 16kb + 4g + r of query row j16
-
-    uint64_t bits = ~0ull;
-    if (en.pidx >= 0) bits = s.bits[buf][wave * 16 + j16] >> (4 * g);
-    // dS = P (dP - D), rounded to bf16 once; value k-step p takes key blocks
-    // 2p (slots 0..3) and 2p+1 (slots 4..7)
-    bf16x8_t DS[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const bool ok0 = (bits >> (16 * kb + r)) & 1ull, ok1 = (bits >> (16 * kb + r + 1)) & 1ull;
-        f32x2_t ds;
-        const float p0 = fast_exp2(__builtin_fmaf(S[kb][r], sl2, -lse_l2));
-        const float p1 = fast_exp2(__builtin_fmaf(S[kb][r + 1], sl2, -lse_l2));
-        ds.x = ok0 ? p0 * (dP[kb][r] - delta) : 0.f;
-        ds.y = ok1 ? p1 * (dP[kb][r + 1] - delta) : 0.f;
-        const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
-        const int slot = 4 * (kb & 1) + r;
-        DS[kb >> 1][slot] = db2.x;
-        DS[kb >> 1][slot + 1] = db2.y;
-      }
-
-    // dQ^T += K^T dS^T (rows = d, columns = queries)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int d4 = 0; d4 < NDB; d4 += 4) {
-        bf16x8_t top[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + 32 * p * D + voff[0][d4 + i]));
-          const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Kt + 32 * p * D + voff[1][d4 + i]));
-          top[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dQacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(top[i], DS[p], dQacc[d4 + i], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
-    e = e_n;
-    kt = kt_n;
-    en = en_n;
-    buf ^= 1;
-  }
-
-  const int ge = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) >> 4;
-  if (q_row < L) {
-    const float c = a.scale;
-    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d0 = db * 16 + 4 * ge;
-      f32x4_t v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = dQacc[db][r] * c;
-      if constexpr (OUT_F32) *(f32x4_t*)((float*)a.dq + out_off + d0) = v;
-      else *(bf16x4_t*)((__bf16*)a.dq + out_off + d0) = __builtin_convertvector(v, bf16x4_t);
-    }
-    if (ge == 0) a.delta[bhL + q_row] = delta;
-  }
-}
 
 // dQ with 32-row waves (v_mfma_f32_32x32x16_bf16): 4 waves own the 128-row
 // query tile and two workgroups share a CU.  Lanes l and l + 32 hold the same

@@ -315,12 +315,12 @@ int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void
 
 int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
                  float scale, void* o, float* lse, void* stream) {
+  if (s && s->in_dtype != AJ_BF16) return AJ_ENOTSUP;  // before any device work
   const void* ins[3] = {q, k, v};
   const void* outs[2] = {o, lse};
   aj::FwdArgs a;
   int32_t st = prepare(s, ins, 3, outs, 2, mask, scale, &a);
   if (st != AJ_OK) return st;
-  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
   a.tq = a.tk = a.tv = nullptr;
   a.to = nullptr;
   return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, false, false,
@@ -330,14 +330,16 @@ int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v,
 int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, const aj_mask_desc* mask, float scale, void* dq, void* dk, void* dv,
                  float* delta, void* stream) {
+  // checks of this entry point first: nothing may reach the device before all pass
+  if (!s || !mask) return AJ_EINVAL;
+  if (!lse || !aligned16(lse)) return AJ_EINVAL;
+  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
+  if (mask->kv_len != mask->seq_len) return AJ_EMASK;
   const void* ins[5] = {q, k, v, o, dout};
   const void* outs[4] = {dq, dk, dv, delta};
   aj::FwdArgs f;
   int32_t st = prepare(s, ins, 5, outs, 4, mask, scale, &f);
   if (st != AJ_OK) return st;
-  if (!lse || !aligned16(lse)) return AJ_EINVAL;
-  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
-  if (mask->kv_len != mask->seq_len) return AJ_EMASK;
   const DeviceTables* t = nullptr;
   st = device_tables(mask, &t);
   if (st != AJ_OK) return st;
@@ -363,12 +365,12 @@ int32_t attn_fwd_kv(const aj_kv_shape* s, const void* q, const void* k, const vo
   const Geometry g{s->batch, s->heads, s->q_len, s->kv_len, s->head_dim, s->in_dtype, s->out_dtype,
                    {s->q_stride_b, s->q_stride_h, s->q_stride_l}, {s->kv_stride_b, s->kv_stride_h, s->kv_stride_l},
                    {s->out_stride_b, s->out_stride_h, s->out_stride_l}};
+  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;  // before any device work
   const void* ins[3] = {q, k, v};
   const void* outs[2] = {o, lse};
   aj::FwdArgs a;
   int32_t st = prepare_geom(g, ins, 3, outs, 2, mask, scale, &a);
   if (st != AJ_OK) return st;
-  if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
   a.tq = a.tk = a.tv = nullptr;
   a.to = nullptr;
   return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, false, false,

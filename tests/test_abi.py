@@ -170,3 +170,81 @@ def test_permuted_output_layout_is_accepted_by_validation():
     d = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16")
     sh = _shape(outs=(64 * 2 * 128, 128, 2 * 128))
     assert _fwd(sh, d.handle) == aj.AJ_EHIP
+
+
+def _primal(shape, desc, ptrs=None, scale=0.125, lse=FAKE):
+    ptrs = ptrs or [FAKE] * 4
+    p = [ctypes.c_void_p(x) if x is not None else None for x in ptrs]
+    return aj.lib().attn_fwd(ctypes.byref(shape) if shape is not None else None, *p[:3], desc,
+                             ctypes.c_float(scale), p[3], ctypes.c_void_p(lse) if lse is not None else None, None)
+
+
+def _bwd(shape, desc, ptrs=None, scale=0.125, lse=FAKE, delta=FAKE):
+    ptrs = ptrs or [FAKE] * 8  # q, k, v, o, dout, dq, dk, dv
+    p = [ctypes.c_void_p(x) if x is not None else None for x in ptrs]
+    return aj.lib().attn_bwd(ctypes.byref(shape) if shape is not None else None, *p[:5],
+                             ctypes.c_void_p(lse) if lse is not None else None, desc, ctypes.c_float(scale),
+                             *p[5:8], ctypes.c_void_p(delta) if delta is not None else None, None)
+
+
+def test_primal_and_gradient_entry_points_reject_bad_arguments():
+    d = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16")
+    df32 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="f32")
+    kv = aj.attn_jvp_mask_desc_from_rects_kv(64, 100, [(0, 64, 0, 100)], head_dim=128, dtype="bf16")
+    h = d.handle
+    assert _primal(None, h) == aj.AJ_EINVAL
+    assert _primal(_shape(), None) == aj.AJ_EINVAL
+    for i in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[i] = None
+        assert _primal(_shape(), h, ptrs) == aj.AJ_EINVAL
+    assert _primal(_shape(), h, lse=None) == aj.AJ_EINVAL
+    assert _primal(_shape(), h, scale=float("nan")) == aj.AJ_EINVAL
+    assert _primal(_shape(idt=aj.AJ_F32, odt=aj.AJ_F32), df32.handle) == aj.AJ_ENOTSUP  # bf16 only
+    assert _primal(_shape(), kv.handle) == aj.AJ_EMASK                                   # key length differs
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert _bwd(_shape(), h, ptrs) == aj.AJ_EINVAL
+    assert _bwd(_shape(), h, lse=None) == aj.AJ_EINVAL
+    assert _bwd(_shape(), h, lse=FAKE + 4) == aj.AJ_EINVAL
+    assert _bwd(_shape(), h, delta=None) == aj.AJ_EINVAL
+    assert _bwd(_shape(), h, scale=0.0) == aj.AJ_EINVAL
+    assert _bwd(_shape(L=80), h) == aj.AJ_EMASK
+    assert _bwd(_shape(idt=aj.AJ_F32, odt=aj.AJ_F32), df32.handle) == aj.AJ_ENOTSUP
+    assert _bwd(_shape(outs=(2 * 64 * 128, 64 * 128, 64)), h) == aj.AJ_EINVAL  # overlapping gradient rows
+
+
+def _kvshape(B=1, H=2, Lq=64, Lk=100, D=128, qs=None, ks=None, os_=None, idt=aj.AJ_BF16, odt=aj.AJ_BF16):
+    qs = qs or (H * Lq * D, Lq * D, D)
+    ks = ks or (H * 4096 * D, 4096 * D, D)
+    os_ = os_ or (H * Lq * D, Lq * D, D)
+    return aj.aj_kv_shape(B, H, Lq, Lk, D, idt, odt, *qs, *ks, *os_)
+
+
+def _fwd_kv(shape, desc, ptrs=None, scale=0.125, lse=FAKE):
+    ptrs = ptrs or [FAKE] * 4
+    p = [ctypes.c_void_p(x) if x is not None else None for x in ptrs]
+    return aj.lib().attn_fwd_kv(ctypes.byref(shape) if shape is not None else None, *p[:3], desc,
+                                ctypes.c_float(scale), p[3], ctypes.c_void_p(lse) if lse is not None else None, None)
+
+
+def test_kv_entry_point_rejects_bad_arguments():
+    kv = aj.attn_jvp_mask_desc_from_rects_kv(64, 100, [(0, 64, 0, 100)], head_dim=128, dtype="bf16")
+    h = kv.handle
+    assert _fwd_kv(None, h) == aj.AJ_EINVAL
+    assert _fwd_kv(_kvshape(), None) == aj.AJ_EINVAL
+    assert _fwd_kv(_kvshape(Lk=101), h) == aj.AJ_EMASK                      # descriptor key length differs
+    assert _fwd_kv(_kvshape(Lq=65), h) == aj.AJ_EMASK
+    assert _fwd_kv(_kvshape(ks=(0, 0, 64)), h) == aj.AJ_EINVAL              # key rows closer than D
+    assert _fwd_kv(_kvshape(ks=(0, 0, 1 << 24)), h) == aj.AJ_EINVAL         # 64 key rows exceed a 31-bit range
+    assert _fwd_kv(_kvshape(qs=(0, 0, 100)), h) == aj.AJ_EINVAL             # not a 16-byte multiple
+    assert _fwd_kv(_kvshape(idt=aj.AJ_F32, odt=aj.AJ_F32), h) == aj.AJ_ENOTSUP  # bf16 only
+
+
+def test_kv_entry_point_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; a valid call would launch")
+    kv = aj.attn_jvp_mask_desc_from_rects_kv(64, 100, [(0, 64, 0, 100)], head_dim=128, dtype="bf16")
+    assert _fwd_kv(_kvshape(), kv.handle) == aj.AJ_EHIP
