@@ -68,15 +68,10 @@ constexpr float kLazyRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2
 // tiles, the 128 per-row key bitmasks) by direct buffer -> LDS DMA into a
 // double buffer: tile t+1 loads while tile t computes.  V and tV are read with
 // gfx950's LDS transpose read.  Rows are unpadded; 16-byte chunk c of row r is
-// stored at position c ^ swz(r), chosen per shape so that every operand read
-// is free of conflicts on the 64-bank LDS:
-//   q16, D = 128: swz(r) = 2 (r % 8) + (r / 8) % 2         (K: one chunk of 16
-//   q16, D =  64: swz(r) = 2 ((r / 2) % 4) + (r / 8) % 2    rows per 16 lanes;
-//                                                           V: two chunks of 8
-//                                                           rows per 32 lanes)
-//   q32, D = 128: swz(r) = 4 (r % 4) + (r / 4) % 4         (K: one chunk of 16
-//   q32, D =  64: swz(r) = 4 ((r / 2) % 2) + (r / 4) % 4    rows; V: four
-//                                                           chunks of 4 rows)
+// stored at position c ^ swz(r), chosen per shape so that the operand reads
+// are free of bank conflicts (swz_q16 / swz_q32 in aj_device.h; the q16
+// D = 128 swizzle serves both the row reads of K and the transpose reads of
+// V, so every tile of a q16 kernel shares one layout).
 
 constexpr int kWavesQ16 = 8;
 constexpr int kWavesQ32 = 4;
@@ -107,7 +102,7 @@ __device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const 
     const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
 #pragma unroll
     for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-      lds_dma_16(lds_addr(dst[Bf16Lds<D, NT>::slot(t)] + (wave + NW * i) * 512), plan.voff[i], rs);
+      lds_dma_16(lds_addr(dst[NT == 4 ? t : t / 2] + (wave + NW * i) * 512), plan.voff[i], rs);
   }
 }
 
