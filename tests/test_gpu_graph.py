@@ -1,0 +1,64 @@
+"""The launch paths under HIP graph capture.
+
+After a first call (which uploads the descriptor's tables), attn_jvp_fwd,
+attn_fwd and attn_bwd enqueue kernels only: no allocation, no memset, no host
+synchronisation.  They are captured into a graph on torch's capture stream and
+the graph is replayed several times, with eager work and synchronisation in
+between; every replay must reproduce the eager results bit for bit (the
+kernels are deterministic).
+"""
+import pytest
+import torch
+
+import attention_jvp_causal_amd as aj
+from attention_jvp_causal_amd.workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "tq", "tk", "tv")
+
+
+def test_jvp_and_gradients_replay_from_a_graph():
+    w = Workload("graph", 1, 2, 128, "bf16", "block_causal", 5, 90, 1, seed=160)
+    dev = {n: t.cuda() for n, t in make_inputs(w).items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    B, H, L, D = w.shape
+    jvp_out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    fwd_out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    bwd_out = tuple(torch.empty((B, H, L, D), dtype=torch.float32, device="cuda") for _ in range(3)) + (
+        torch.empty((B, H, L), dtype=torch.float32, device="cuda"),)
+    g = torch.Generator().manual_seed(3)
+    d_out = torch.randn(w.shape, generator=g).to(torch.bfloat16).cuda()
+
+    def run():
+        aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, scale=w.scale, out=jvp_out)
+        aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc, scale=w.scale, out=fwd_out)
+        aj.attn_bwd(dev["q"], dev["k"], dev["v"], fwd_out[0], d_out, fwd_out[1], desc, scale=w.scale,
+                    out_dtype=torch.float32, out=bwd_out)
+
+    run()  # eager; uploads the tables
+    torch.cuda.synchronize()
+    want = [t.clone() for t in jvp_out + fwd_out + bwd_out]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for t in jvp_out + fwd_out + bwd_out:
+            t.fill_(float("nan"))  # eager, outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in jvp_out + fwd_out + bwd_out:
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(jvp_out + fwd_out + bwd_out, want):
+            assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
