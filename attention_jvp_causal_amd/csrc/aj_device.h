@@ -113,6 +113,25 @@ struct TileLoadPlan {
   }
 };
 
+// Workgroup index -> (task rank, flattened head b * H + h).  The B * H heads
+// are taken in groups of G: all workgroups of one group come before those of
+// the next, so only G heads' keys are being streamed at any time, and inside a
+// group consecutive workgroups cycle through its heads, task rank outer.  The
+// dispatcher deals workgroups to the eight XCDs in turn, so with G dividing 8
+// each XCD, and its L2, serves one head of the group.  G = B * H is the plain
+// rank-major order.
+struct TaskCoord {
+  int rank, bh;
+};
+__device__ __forceinline__ TaskCoord task_coord(int idx, int n_tasks, int BH, int G) {
+  const int per = G * n_tasks;
+  const int grp = idx / per;
+  const int rem = idx - grp * per;
+  const int gsz = min(G, BH - grp * G);
+  const int rank = rem / gsz;
+  return {rank, grp * G + (rem - rank * gsz)};
+}
+
 // Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx.
 __device__ __forceinline__ void issue_bits_load(uint64_t* dst, const uint64_t* bits, int pidx, int lane) {
   lds_dma_16(lds_addr(dst), uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));

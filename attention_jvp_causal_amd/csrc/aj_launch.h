@@ -24,6 +24,7 @@ struct FwdArgs {
   int64_t osb, osh, osl;  // output strides (elements)
   int32_t B, H, L, n_tasks;
   int32_t Lk;             // key length (= L except for the KV-cache forward)
+  int32_t head_group;     // heads whose workgroups are interleaved (set by launch_fwd)
   float scale;       // softmax scale c
   float scale_log2;  // c * log2(e)
   const int32_t* qt_off;
@@ -49,20 +50,30 @@ struct BwdArgs {
   int64_t isb, ish, isl;
   int64_t osb, osh, osl;
   int32_t B, H, L, n_row_tasks, n_col_tasks;
+  int32_t head_group;  // set by launch_bwd
   float scale;
   float scale_log2;
   DeviceMap rows;  // query tiles -> key-tile runs
   DeviceMap cols;  // key tiles -> query-tile runs
 };
 
+// Number of heads whose workgroups are interleaved (the grouping of
+// task_coord): one head per XCD.  Each XCD then runs 32 (q16) or 64 (q32)
+// query tiles of one head at a time, taken longest-first, so tiles of equal
+// key range start together and stream the same key tiles through that XCD's
+// L2 at about the same time.  Smaller groups leave a tail: the last group's
+// longest tiles start late.
+constexpr int32_t kHeadGroup = 8;
+inline int32_t head_group_for(int32_t BH) { return BH < kHeadGroup ? BH : kHeadGroup; }
+
 // Enqueues the dQ kernel and then the dK / dV kernel on `stream`.
-int launch_bwd(const BwdArgs& a, int out_dtype, int head_dim, hipStream_t stream);
+int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream);
 
 // Enqueues the forward kernel; returns an aj_status.  jvp = false computes
 // only O and lse (tq, tk, tv and to are not used).  variants = true when the
 // descriptor declares tangent-free tiles: the kernel instance that skips
 // their zero products runs instead of the plain one.
-int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
+int launch_fwd(FwdArgs a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
                hipStream_t stream);
 
 }  // namespace aj

@@ -107,7 +107,8 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_row_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int qt = a.rows.tasks[rank];
   const int L = a.L;
@@ -281,7 +282,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
   const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_col_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int ktile = a.cols.tasks[rank];
   const int L = a.L;
@@ -492,9 +494,10 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                      stream, a);
 }
 
-int launch_bwd(const BwdArgs& a, int out_dtype, int head_dim, hipStream_t stream) {
+int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream) {
   const int64_t g1 = int64_t(a.n_row_tasks) * a.B * a.H, g2 = int64_t(a.n_col_tasks) * a.B * a.H;
   if (g1 <= 0 || g2 <= 0 || g1 > 0x7fffffff || g2 > 0x7fffffff) return AJ_EINVAL;
+  a.head_group = head_group_for(a.B * a.H);
   const bool f32 = out_dtype == AJ_F32;
   if (head_dim == 128) {
     if (f32) launch_bwd_d<128, true>(a, stream);

@@ -120,7 +120,8 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
   const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int qt = a.tasks[rank];
   const int L = a.L;
@@ -443,7 +444,8 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int qt = a.tasks[rank];
   const int L = a.L;
@@ -759,7 +761,8 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int qt = a.tasks[rank];
   const int L = a.L;
@@ -912,10 +915,11 @@ static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid,
   }
 }
 
-int launch_fwd(const FwdArgs& a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
+int launch_fwd(FwdArgs a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
                hipStream_t stream) {
   const int64_t grid64 = int64_t(a.n_tasks) * a.B * a.H;
   if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
+  a.head_group = head_group_for(a.B * a.H);
   const dim3 grid((unsigned)grid64);
   if (in_dtype == AJ_BF16) {
     if (!jvp) launch_bf16<false, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);

@@ -96,3 +96,30 @@ def test_single_token(dt):
     # one key: O = v, tO = tv exactly up to output rounding
     np.testing.assert_allclose(to_np(got[0]), x["v"], rtol=1e-2, atol=1e-2)
     np.testing.assert_allclose(to_np(got[1]), x["tv"], rtol=1e-2, atol=1e-2)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_head_groups_with_a_ragged_last_group(D):
+    # Workgroups are taken eight heads at a time; B x H = 21 leaves a last
+    # group of 5 heads, and 3 query tiles per head make several ranks per head.
+    w = Workload("hgroups", 3, 7, D, "bf16", "block_causal", 3, 100, 1, seed=155)
+    print(f"[case] head groups B={w.batch} H={w.heads} L={w.seq_len} D={D}", flush=True)
+    inputs, desc, got = run_gpu(w)
+    x = as_float64(inputs)
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale)
+    compare(w, [to_np(t) for t in got], ref, label=f"hgroups_{D}")
+    # the primal forward and the gradients walk the same grid order
+    from oracle import attn_vjp_ref
+
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    o, lse = aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc, scale=w.scale)
+    g = torch.Generator().manual_seed(156)
+    d_out = torch.randn(w.shape, generator=g).to(torch.bfloat16)
+    dq, dk, dv, _ = aj.attn_bwd(dev["q"], dev["k"], dev["v"], o, d_out.cuda(), lse, desc, scale=w.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(lse), ref[2], rtol=0, atol=1e-2)
+    gref = attn_vjp_ref(x["q"], x["k"], x["v"], d_out.double().numpy(), oracle_mask(w), scale=w.scale)
+    for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), gref):
+        t = to_np(t)
+        err = np.linalg.norm(t - r) / np.linalg.norm(r)
+        assert err <= 1e-2, f"hgroups_{D} {name}: rel-L2 {err:.3e}"
