@@ -65,8 +65,9 @@ constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer resource: 32-bit data
 // One direct buffer -> LDS load of 16 bytes per lane: lane l's chunk lands at
 // LDS byte address lds_base + 16 l.  Written as inline asm so that the
 // compiler does not track it: the kernel waits for these loads itself
-// (wait_vmcnt) right before the barrier that publishes a buffer, instead of
-// the compiler's conservative wait for every load in flight into any buffer.
+// (wait_vmcnt) right before the barrier that publishes a buffer.  The
+// compiler cannot tell the two buffers apart and would wait for the next
+// tile's loads before the first read of the current one.
 // The instruction has no register results; it only writes LDS.  m0 is set
 // here and used by nothing else in these kernels (checked by a build test).
 __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, uint32_t voffset, i32x4_t rsrc) {
@@ -101,7 +102,6 @@ template <int NW, int D>
 struct TileLoadPlan {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int NI = (BN * CH) / (64 * NW);   // wave instructions per tensor
-  static constexpr int PER_TILE = 4 * NI;            // DMA instructions per wave per tile
   uint32_t voff[NI];
   __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int)) {
 #pragma unroll

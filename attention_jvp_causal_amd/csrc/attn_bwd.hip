@@ -102,7 +102,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqW
 void attn_bwd_dq32_kernel(BwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for S^T and dP^T
   constexpr int NDB = D / 32;  // 32-row blocks of d for dQ^T
-  constexpr int NL = 2 * TileLoadPlan<kDqWaves32, D>::NI;
   __shared__ __attribute__((aligned(1024))) KvLds<D> s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -187,14 +186,10 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
         kt_n = en_n.kt0;
       }
     }
-    if (e_n < e1) {
-      prefetch(buf ^ 1, en_n, kt_n);
-      if (en_n.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
-      else wait_vmcnt<NL>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // one barrier per tile (loads landed; other buffer free for the next DMA)
+    wait_vmcnt<0>();
     __syncthreads();
+    if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
     const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
     const uint16_t* Kt = s.t[buf][0];
     const uint16_t* Vt = s.t[buf][1];
@@ -245,7 +240,6 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();
     e = e_n;
     kt = kt_n;
     en = en_n;
@@ -277,7 +271,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdW
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int NL = 2 * TileLoadPlan<kBwdWaves, D>::NI;
   __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
@@ -321,11 +314,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.cols.bits, x.pidx, lane);
   };
-  auto wait_all_but = [&](const Entry& x) {
-    if (wave == 1) wait_vmcnt<NL + 2>();
-    else if (x.pidx >= 0 && wave == 0) wait_vmcnt<NL + 1>();
-    else wait_vmcnt<NL>();
-  };
   const int e0 = a.cols.qt_off[ktile], e1 = a.cols.qt_off[ktile + 1];
   int e = e0, qtl = 0;
   Entry en = {0, 0, -1, 0};
@@ -367,13 +355,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         qt_n = en_n.kt0;
       }
     }
-    if (e_n < e1) {
-      prefetch(buf ^ 1, en_n, qt_n);
-      wait_all_but(en_n);
-    } else {
-      wait_vmcnt<0>();
-    }
+    // one barrier per tile (loads landed; other buffer free for the next DMA)
+    wait_vmcnt<0>();
     __syncthreads();
+    if (e_n < e1) prefetch(buf ^ 1, en_n, qt_n);
     const uint16_t* Qt = s.t[buf][0];
     const uint16_t* dOt = s.t[buf][1];
 
@@ -452,7 +437,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
           dKacc[d4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtop[i], DS[p], dKacc[d4 + i], 0, 0, 0);
       }
     }
-    __syncthreads();
     e = e_n;
     qtl = qt_n;
     en = en_n;

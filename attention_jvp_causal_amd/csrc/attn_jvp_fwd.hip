@@ -113,8 +113,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ16, 64 * kWave
 void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   constexpr int NKS = D / 32;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 16;  // 16-row blocks of d for the value products
-  constexpr int NL_ALL = TileLoadPlan<kWavesQ16, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
-  constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
   using Lds = Bf16Lds<D, 4>;
   __shared__ __attribute__((aligned(1024))) Lds s;
 
@@ -157,17 +155,6 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     else
       issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
-  };
-  // wait until at most the loads of x's tile (issued last) are in flight
-  auto wait_all_but = [&](const Entry& x) {
-    const bool bl = x.pidx >= 0 && wave == 0;
-    if (JVP && (!VARIANTS || x.flags == kTileJvp)) {
-      if (bl) wait_vmcnt<NL_ALL + 1>();
-      else wait_vmcnt<NL_ALL>();
-    } else {
-      if (bl) wait_vmcnt<NL_KV + 1>();
-      else wait_vmcnt<NL_KV>();
-    }
   };
 
   const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
@@ -364,7 +351,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   };
 
   while (e < e1) {
-    // next key tile into the other buffer while this one is computed
+    // next key tile, loaded into the other buffer while this one is computed
     int e_n = e, kt_n = kt + 1;
     Entry en_n = en;
     if (kt_n >= en.kt1) {
@@ -374,13 +361,12 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
         kt_n = en_n.kt0;
       }
     }
-    if (e_n < e1) {
-      prefetch(buf ^ 1, en_n, kt_n);
-      wait_all_but(en_n);
-    } else {
-      wait_vmcnt<0>();
-    }
+    // One barrier per tile: after it, every wave's loads of this tile have
+    // landed and every wave is done with the other buffer, which the next
+    // tile's DMA then refills.
+    wait_vmcnt<0>();
     __syncthreads();
+    if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
     if constexpr (!JVP) {
       tile(std::integral_constant<int, kTileAllFree>{});
     } else if constexpr (!VARIANTS) {
@@ -391,7 +377,6 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       else if (var == kTileKeysFree) tile(std::integral_constant<int, kTileKeysFree>{});
       else tile(std::integral_constant<int, kTileAllFree>{});
     }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
     e = e_n;
     kt = kt_n;
     en = en_n;
@@ -436,8 +421,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWave
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
-  constexpr int NL_ALL = TileLoadPlan<kWavesQ32, D>::PER_TILE;  // DMA per wave: K, tK, V, tV
-  constexpr int NL_KV = NL_ALL / 2;                              // DMA per wave: K, V
   constexpr int NT = JVP ? 4 : 2;
   using Lds = Bf16Lds<D, NT>;
   __shared__ __attribute__((aligned(1024))) Lds s;
@@ -469,16 +452,6 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     else
       issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
-  };
-  auto wait_all_but = [&](const Entry& x) {
-    const bool bl = x.pidx >= 0 && wave == 0;
-    if (JVP) {
-      if (bl) wait_vmcnt<NL_ALL + 1>();
-      else wait_vmcnt<NL_ALL>();
-    } else {
-      if (bl) wait_vmcnt<NL_KV + 1>();
-      else wait_vmcnt<NL_KV>();
-    }
   };
 
   // first key tile in flight before the prologue
@@ -656,7 +629,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   };
 
   while (e < e1) {
-    // next key tile into the other buffer while this one is computed
+    // next key tile, loaded into the other buffer while this one is computed
     int e_n = e, kt_n = kt + 1;
     Entry en_n = en;
     if (kt_n >= en.kt1) {
@@ -666,16 +639,14 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
         kt_n = en_n.kt0;
       }
     }
-    if (e_n < e1) {
-      prefetch(buf ^ 1, en_n, kt_n);
-      wait_all_but(en_n);
-    } else {
-      wait_vmcnt<0>();
-    }
+    // One barrier per tile: after it, every wave's loads of this tile have
+    // landed and every wave is done with the other buffer, which the next
+    // tile's DMA then refills.
+    wait_vmcnt<0>();
     __syncthreads();
+    if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
     if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{});
     else tile(std::integral_constant<int, kTileJvp>{});
-    __syncthreads();  // every wave is done with this buffer before it is refilled
     e = e_n;
     kt = kt_n;
     en = en_n;
