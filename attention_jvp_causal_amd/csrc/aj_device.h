@@ -132,6 +132,23 @@ __device__ __forceinline__ TaskCoord task_coord(int idx, int n_tasks, int BH, in
   return {rank, grp * G + (rem - rank * gsz)};
 }
 
+// DMA of rows [row0, row0 + BN) of two [L, D] tensors into dst[0] and
+// dst[1] (rows past L read as zero).
+template <int NW, int D>
+__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
+                                                 const uint16_t* s0, const uint16_t* s1, int64_t sl, int row0, int L,
+                                                 int wave) {
+  const int nrec = int((int64_t)min(L - row0, BN) * sl * 2);
+  const i32x4_t r0 = make_rsrc(s0 + (int64_t)row0 * sl, nrec);
+  const i32x4_t r1 = make_rsrc(s1 + (int64_t)row0 * sl, nrec);
+#pragma unroll
+  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[0] + (wave + NW * i) * 512), plan.voff[i], r0);
+#pragma unroll
+  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+    lds_dma_16(lds_addr(dst[1] + (wave + NW * i) * 512), plan.voff[i], r1);
+}
+
 // Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx.
 __device__ __forceinline__ void issue_bits_load(uint64_t* dst, const uint64_t* bits, int pidx, int lane) {
   lds_dma_16(lds_addr(dst), uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));

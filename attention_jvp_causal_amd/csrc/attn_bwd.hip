@@ -66,22 +66,6 @@ __device__ __forceinline__ void lds_dma_4(uint32_t lds_base, uint32_t voffset, i
       : "memory", "m0");
 }
 
-// DMA of rows [row0, row0 + BN) of two [L, D] tensors into one LDS buffer.
-template <int NW, int D>
-__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
-                                                 const uint16_t* s0, const uint16_t* s1, int64_t sl, int row0, int L,
-                                                 int wave) {
-  const int nrec = int((int64_t)min(L - row0, BN) * sl * 2);
-  const i32x4_t r0 = make_rsrc(s0 + (int64_t)row0 * sl, nrec);
-  const i32x4_t r1 = make_rsrc(s1 + (int64_t)row0 * sl, nrec);
-#pragma unroll
-  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[0] + (wave + NW * i) * 512), plan.voff[i], r0);
-#pragma unroll
-  for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[1] + (wave + NW * i) * 512), plan.voff[i], r1);
-}
-
 __device__ __forceinline__ float bf16_dot8(bf16x8_t x, bf16x8_t y, float acc) {
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
@@ -334,15 +318,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
   const int vrow = 4 * g + (j16 >> 2);
-  int voff[2][NDB];
+  // The second read of a pair is 16 rows further on, at the same swizzle
+  // (swz_q16 depends on the row mod 16): a constant offset of 16 D.
+  int voff[NDB];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int row = vrow + 16 * h;
-      const int chunk = 2 * db + ((j16 & 3) >> 1);
-      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
-    }
+  for (int db = 0; db < NDB; ++db) {
+    const int chunk = 2 * db + ((j16 & 3) >> 1);
+    voff[db] = vrow * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
+  }
 
   int buf = 0;
   while (e < e1) {
@@ -420,8 +403,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         bf16x8_t oop[4], qtop[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int off_a = 32 * p * D + voff[0][d4 + i];
-          const int off_b = 32 * p * D + voff[1][d4 + i];
+          const int off_a = 32 * p * D + voff[d4 + i];
+          const int off_b = off_a + 16 * D;
           const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_a));
           const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_b));
           const s16x4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Qt + off_a));

@@ -187,15 +187,14 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   // second read) and d = 16db + 4(j16%4), i.e. logical chunk 2db + (j16%4)/2,
   // half j16 % 2.  swz depends on the row mod 16, which 32p and 16 keep.
   const int vrow = 4 * g + (j16 >> 2);
-  int voff[2][NDB];
+  // The second read of a pair is 16 rows further on, at the same swizzle
+  // (swz_q16 depends on the row mod 16): a constant offset of 16 D.
+  int voff[NDB];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int row = vrow + 16 * h;
-      const int chunk = 2 * db + ((j16 & 3) >> 1);
-      voff[h][db] = row * D + ((chunk ^ swz_q16<D>(row)) << 3) + 4 * (j16 & 1);
-    }
+  for (int db = 0; db < NDB; ++db) {
+    const int chunk = 2 * db + ((j16 & 3) >> 1);
+    voff[db] = vrow * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
+  }
 
   int buf = 0;
 
@@ -321,8 +320,8 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
         bf16x8_t vop[4], tvop[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int off_a = 32 * p * D + voff[0][d4 + i];
-          const int off_b = 32 * p * D + voff[1][d4 + i];
+          const int off_a = 32 * p * D + voff[d4 + i];
+          const int off_b = off_a + 16 * D;
           const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
           const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
           s16x4_t ta, tb;
