@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <type_traits>
 
 #include "aj_device.h"
@@ -415,7 +416,12 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
 
 // ---- q32 shape --------------------------------------------------------------
 
-template <int D, bool OUT_F32, bool JVP>
+// SCALE_IN_Q: the scale is a power of two in (0, 1] and is folded into the Q
+// and tQ registers (exact: a power-of-two multiple of a bf16 value is a bf16
+// value, and every fp32 partial sum of the score products scales with it), so
+// the MFMAs deliver c s and c ts and u = p~ (c ts) takes one multiply less.
+// The results are bit for bit those of the unfolded kernel.
+template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32), amdgpu_waves_per_eu(2, 2)))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
@@ -478,6 +484,14 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   // Q, tQ and the first key tile have landed; nothing the compiler tracks is
   // in flight inside the loop below.
   wait_vmcnt<0>();
+  if constexpr (SCALE_IN_Q) {
+    typedef float f32x8_t __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      Qr[kk] = __builtin_convertvector(__builtin_convertvector(Qr[kk], f32x8_t) * a.scale, bf16x8_t);
+      tQr[kk] = __builtin_convertvector(__builtin_convertvector(tQr[kk], f32x8_t) * a.scale, bf16x8_t);
+    }
+  }
 
   f32x16_t Oacc[NDB], ABacc[NDB];
 #pragma unroll
@@ -486,7 +500,8 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
   float m_run = -INFINITY;            // reference max (log2 units, scale folded in)
   float l_part = 0.f, mu_part = 0.f;  // this lane's half of the row sums
-  const float sl2 = a.scale_log2, c = a.scale;
+  // log2(e) and 1 when the scale is already in the scores
+  const float sl2 = SCALE_IN_Q ? 1.44269504088896340736f : a.scale_log2, c = SCALE_IN_Q ? 1.0f : a.scale;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   int koff[NKK];
@@ -880,6 +895,17 @@ static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid,
     if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, JVP, VARIANTS>), grid, b16, 0, stream, a);
     else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, JVP, VARIANTS>), grid, b16, 0, stream, a);
   } else {
+    // the JVP with a power-of-two scale (1/8 is the usual one at d = 64):
+    // the scale folded into Q and tQ
+    int e2 = 0;
+    const bool pow2 = a.scale > 0.f && a.scale <= 1.f && std::frexp(a.scale, &e2) == 0.5f;
+    if constexpr (JVP) {
+      if (pow2) {
+        if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true>), grid, b32, 0, stream, a);
+        else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, true>), grid, b32, 0, stream, a);
+        return;
+      }
+    }
     if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, JVP>), grid, b32, 0, stream, a);
     else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, JVP>), grid, b32, 0, stream, a);
   }

@@ -163,3 +163,27 @@ def test_strided_inputs_and_outputs():
     x = as_float64(inputs)
     ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w))
     compare(w, [to_np(o), to_np(to), to_np(lse)], ref, label="strided")
+
+
+@pytest.mark.parametrize("D,scale", [(64, 0.1), (64, 0.25), (64, 1.0 / 8), (128, 1.0 / 8)])
+def test_scales(D, scale):
+    # At d = 64 a power-of-two scale is folded into Q and tQ inside the kernel
+    # (bit for bit the unfolded arithmetic); other scales take the general
+    # path.  Both against the oracle, plus the folded JVP's O and lse against
+    # the primal forward, which never folds: equal bit for bit.
+    import attention_jvp_causal_amd as aj
+
+    w = Workload(f"scale_{D}_{scale}", 1, 2, D, "bf16", "block_causal", 5, 70, 2, seed=160)
+    inputs = make_inputs(w)
+    dev = {n: t.cuda() for n, t in inputs.items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=D, dtype="bf16")
+    print(f"[case] scale={scale} D={D}", flush=True)
+    o, to, lse = aj.attn_jvp_fwd(*(dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")), desc, scale=scale)
+    o2, lse2 = aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc, scale=scale)
+    torch.cuda.synchronize()
+    if D == 64:
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    x = as_float64(inputs)
+    ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=scale)
+    compare(w, [to_np(o), to_np(to), to_np(lse)], ref, label=w.name)
