@@ -82,6 +82,13 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("stress_chunk3_d64", 2, 24, 64, "bf16", MASK_BLOCK_CAUSAL, 21, 880, 3, seed=5,
                  sigma_qk=3.0, sigma_v=1.0, sigma_t=0.5,
                  notes="online-softmax stress: large logits, 7 chunks x 3 x 880 tokens, d=64"),
+        # One GPU's share under head-parallel (Ulysses) sequence sharding over 4
+        # GPUs: 3 of the 12 heads at the full sequence length.
+        Workload("wan13b_chunk3_causal_h3", 1, 3, 128, "bf16", MASK_BLOCK_CAUSAL, 21, 1560, 3, seed=6,
+                 notes="c3-3 at 3 heads: one GPU's share of the 12 heads over 4 GPUs"),
+        Workload("wan13b_tf_clean_noisy_h3", 1, 3, 128, "bf16", MASK_TF_CLEAN_NOISY, 21, 1560, 1, seed=7,
+                 clean_tangent_zero=True,
+                 notes="teacher forcing at 3 heads: one GPU's share of the 12 heads over 4 GPUs"),
     ]
 }
 

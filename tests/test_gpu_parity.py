@@ -64,7 +64,7 @@ def test_bf16_inputs_fp32_outputs(case):
 
 
 @pytest.mark.parametrize("wname", ["wan13b_frame_causal", "wan13b_chunk3_causal", "wan13b_tf_clean_noisy",
-                                   "stress_chunk3_d64"])
+                                   "stress_chunk3_d64", "wan13b_chunk3_causal_h3"])
 def test_full_size_workloads_sampled_rows(wname):
     w = WORKLOADS[wname]
     print(f"[case] full-size {wname} shape={w.shape} {w.dtype}", flush=True)
