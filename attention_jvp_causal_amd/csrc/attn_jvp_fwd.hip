@@ -5,15 +5,16 @@
 // streaming only the admissible key tiles of the mask; the same tile schedule
 // serves the scores and their tangents.
 //
-// Work decomposition.  A workgroup (4 waves, 256 lanes) owns one 128-row query
-// tile of one (batch, head); wave w owns query rows 32w..32w+31 of that tile.
-// Keys stream in tiles of 64 through LDS.  Per key tile and wave:
-//   S^T  = K Q^T             (keys x queries, MFMA 32x32x16 bf16, fp32 acc)
+// Work decomposition.  A workgroup owns one 128-row query tile of one (batch,
+// head), split into 16-row waves (8 per workgroup) or 32-row waves (4 per
+// workgroup); the shapes are described below.  Keys stream in tiles of 64
+// through LDS.  Per key tile and wave:
+//   S^T  = K Q^T             (keys x queries, bf16 MFMA, fp32 accumulation)
 //   tS^T = tK Q^T + K tQ^T   (one accumulator chain)
-// Computing the transposed scores puts one query row in each lane (lanes l and
-// l+32 share a row and split its keys), so the softmax statistics are per lane
-// and the accumulator registers feed the next MFMA as its B operand without any
-// data movement:
+// Computing the transposed scores puts each query row in one lane column (the
+// lanes of a column split its keys), so the softmax statistics are per lane up
+// to a cross-lane exchange, and the accumulator registers feed the next MFMA
+// as its B operand without any data movement:
 //   O~^T += V^T P~^T        (A + B)^T += V^T (P~ . tS)^T + tV^T P~^T
 // V and tV are read from LDS with transpose reads.
 //
