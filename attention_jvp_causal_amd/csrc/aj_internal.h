@@ -56,6 +56,11 @@ struct TileMap {
   std::vector<int32_t> qt_off;      // n_qt + 1 offsets into entries
   std::vector<Entry> entries;
   std::vector<int32_t> tasks;       // owner tiles, most work first
+  // The same tasks split by class, each part most work first: first the
+  // owner tiles whose every span is kTileAllFree (or that have none: nothing
+  // of the JVP but the primal remains), n_primal_tasks of them, then the rest.
+  std::vector<int32_t> tasks_split;
+  int32_t n_primal_tasks = 0;
   std::vector<uint64_t> bits;       // partial_tiles * kTileM words
 };
 
@@ -63,6 +68,7 @@ struct DeviceMap {
   const int32_t* qt_off = nullptr;
   const Entry* entries = nullptr;
   const int32_t* tasks = nullptr;
+  const int32_t* tasks_split = nullptr;
   const uint64_t* bits = nullptr;
 };
 

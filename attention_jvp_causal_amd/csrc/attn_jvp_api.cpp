@@ -34,7 +34,7 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
     return AJ_OK;
   }
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  // layout: [rows map | cols map], each {qt_off | entries | tasks | bits}
+  // layout: [rows map | cols map], each {qt_off | entries | tasks | tasks_split | bits}
   struct Part {
     const void* src;
     size_t bytes, off;
@@ -49,6 +49,7 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
     add(m->qt_off.data(), m->qt_off.size() * sizeof(int32_t));
     add(m->entries.data(), m->entries.size() * sizeof(Entry));
     add(m->tasks.data(), m->tasks.size() * sizeof(int32_t));
+    add(m->tasks_split.data(), m->tasks_split.size() * sizeof(int32_t));
     add(m->bits.data(), m->bits.size() * sizeof(uint64_t));
   }
   std::vector<uint8_t> host(total, 0);
@@ -63,10 +64,11 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
   uint8_t* b = static_cast<uint8_t*>(base);
   aj::DeviceMap* dm[2] = {&t.rows, &t.cols};
   for (int i = 0; i < 2; ++i) {
-    dm[i]->qt_off = reinterpret_cast<const int32_t*>(b + parts[4 * i].off);
-    dm[i]->entries = reinterpret_cast<const Entry*>(b + parts[4 * i + 1].off);
-    dm[i]->tasks = reinterpret_cast<const int32_t*>(b + parts[4 * i + 2].off);
-    dm[i]->bits = reinterpret_cast<const uint64_t*>(b + parts[4 * i + 3].off);
+    dm[i]->qt_off = reinterpret_cast<const int32_t*>(b + parts[5 * i].off);
+    dm[i]->entries = reinterpret_cast<const Entry*>(b + parts[5 * i + 1].off);
+    dm[i]->tasks = reinterpret_cast<const int32_t*>(b + parts[5 * i + 2].off);
+    dm[i]->tasks_split = reinterpret_cast<const int32_t*>(b + parts[5 * i + 3].off);
+    dm[i]->bits = reinterpret_cast<const uint64_t*>(b + parts[5 * i + 4].off);
   }
   t.base = base;
   *out = &t;
@@ -309,8 +311,31 @@ int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void
   if (st != AJ_OK) return st;
   a.tq = tq; a.tk = tk; a.tv = tv; a.to = to;
   const bool variants = mask->rows.pairs_by_var[1] + mask->rows.pairs_by_var[2] > 0;
-  return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, true, variants,
-                        static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!variants || s->in_dtype != AJ_BF16)
+    return aj::launch_fwd(a, s->in_dtype, s->out_dtype, s->head_dim, true, variants, hs);
+  // Tangent-free declarations: the query tiles left with only primal work
+  // (every span tangent-free, or none) run the primal kernel, which writes
+  // tO = 0 for them; the others run the JVP kernel.  Two launches in stream
+  // order over disjoint rows.
+  const DeviceTables* t = nullptr;
+  st = device_tables(mask, &t);
+  if (st != AJ_OK) return st;
+  const int32_t np = mask->rows.n_primal_tasks, nq = mask->rows.n_qt;
+  if (np > 0) {
+    aj::FwdArgs p = a;
+    p.tasks = t->rows.tasks_split;
+    p.n_tasks = np;
+    st = aj::launch_fwd(p, s->in_dtype, s->out_dtype, s->head_dim, false, false, hs);
+    if (st != AJ_OK) return st;
+  }
+  if (nq > np) {
+    aj::FwdArgs r = a;
+    r.tasks = t->rows.tasks_split + np;
+    r.n_tasks = nq - np;
+    st = aj::launch_fwd(r, s->in_dtype, s->out_dtype, s->head_dim, true, variants, hs);
+  }
+  return st;
 }
 
 int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,

@@ -694,6 +694,13 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
           *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
           if constexpr (JVP) *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
         }
+        // primal rows of a JVP call (all their tangents declared zero): tO = 0
+        if constexpr (!JVP) {
+          if (a.to) {
+            if constexpr (OUT_F32) *(f32x4_t*)((float*)a.to + out_off + d0) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            else *(u32x2_t*)((__bf16*)a.to + out_off + d0) = u32x2_t{0u, 0u};
+          }
+        }
       }
     if (hi == 0)
       a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;

@@ -234,6 +234,17 @@ static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const
   std::stable_sort(m->tasks.begin(), m->tasks.end(), [&](int32_t x, int32_t y) {
     return work[x] != work[y] ? work[x] > work[y] : x > y;
   });
+  auto primal_only = [&](int32_t qt) {
+    for (int32_t e = m->qt_off[qt]; e < m->qt_off[qt + 1]; ++e)
+      if (m->entries[e].flags != kTileAllFree) return false;
+    return true;
+  };
+  m->tasks_split.clear();
+  for (int32_t qt : m->tasks)
+    if (primal_only(qt)) m->tasks_split.push_back(qt);
+  m->n_primal_tasks = int32_t(m->tasks_split.size());
+  for (int32_t qt : m->tasks)
+    if (!primal_only(qt)) m->tasks_split.push_back(qt);
 }
 
 int32_t build_from_rects(int32_t Lq, int32_t Lk, const int32_t* r, int32_t n, int32_t head_dim, int32_t dtype,

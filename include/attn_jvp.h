@@ -141,10 +141,15 @@ int32_t attn_jvp_mask_desc_from_rects_kv(int32_t q_len, int32_t kv_len, const in
  * and tv are exactly zero at these tokens (for every batch and head); the
  * kernel then skips the products that are zero, per tile of 128 queries x 64
  * keys that lies entirely inside the ranges, and need not read those
- * tangents.  The result equals attn_jvp_fwd with the plain descriptor
- * whenever the declaration holds; if it does not, the tangent output is
- * unspecified.  Host-only.  Errors: AJ_EINVAL (null pointers, bad range),
- * AJ_ENOMEM.  On error *out is set to NULL. */
+ * tangents.  Query tiles left with only primal work (all the tiles they visit
+ * lie inside the ranges) run the primal forward of attn_fwd, which writes
+ * tO = 0 for them, in a launch of their own before the JVP kernel's.  The
+ * result equals attn_jvp_fwd with the plain descriptor whenever the
+ * declaration holds: bit for bit, except that at head_dim 128 O and lse of
+ * the primal-only query tiles agree to rounding (as attn_fwd's do); if the
+ * declaration does not hold, the tangent output is unspecified.  Host-only.
+ * Errors: AJ_EINVAL (null pointers, bad range), AJ_ENOMEM.  On error *out is
+ * set to NULL. */
 int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t* ranges, int32_t n_ranges,
                                         aj_mask_desc** out);
 

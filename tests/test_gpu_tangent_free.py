@@ -1,9 +1,14 @@
 """HIP JVP with tangent-free token ranges (the clean-context fast path) vs the
-fp64 oracle and vs the same kernel without the declaration.
+fp64 oracle and vs the same call without the declaration.
 
 When the declared tangents are zero, the skipped products only ever add exact
-zeros, so O and lse must be bitwise identical to the plain descriptor's run
-and tO equal in value; against the oracle the usual tolerances apply.
+zeros.  Query tiles that keep some tangent work run the JVP kernel's variant
+instance: their O and lse are bitwise those of the plain descriptor's run.
+Query tiles left with only primal work run the primal forward kernel (tO = 0
+written): bitwise equal at d = 64, where it is the JVP kernel's own code, and
+equal to rounding at d = 128 (32-row instead of 16-row waves, as for
+attn_fwd).  tO is equal in value everywhere; against the oracle the usual
+tolerances apply.
 """
 import numpy as np
 import pytest
@@ -25,11 +30,37 @@ def _run(dev, desc, out_dtype=None):
     return r
 
 
-def _same_as_plain(fast, plain, label):
-    assert torch.equal(fast[0], plain[0]), f"{label}: O differs from the plain descriptor's"
-    assert torch.equal(fast[2], plain[2]), f"{label}: lse differs from the plain descriptor's"
+def _primal_rows(desc):
+    """Rows of the query tiles whose visited tiles are all tangent-free (read
+    from the descriptor's tile variants)."""
+    L, tm, tn = desc.seq_len, 128, 64
+    n_kt = (desc.kv_len + tn - 1) // tn
+    rows = torch.zeros(L, dtype=torch.bool)
+    for qt in range((L + tm - 1) // tm):
+        if all(desc.tile_variant(qt, kt) in (-1, 3) for kt in range(n_kt)):
+            rows[qt * tm:(qt + 1) * tm] = True
+    return rows
+
+
+def _same_as_plain(fast, plain, label, desc):
     # equal in value (a zero may differ in sign)
     assert bool((fast[1] == plain[1]).all()), f"{label}: tO differs from the plain descriptor's"
+    pr = _primal_rows(desc).to(fast[0].device)
+    jr = ~pr
+    assert torch.equal(fast[0][:, :, jr], plain[0][:, :, jr]), f"{label}: O differs on the JVP rows"
+    assert torch.equal(fast[2][:, :, jr], plain[2][:, :, jr]), f"{label}: lse differs on the JVP rows"
+    if not bool(pr.any()):
+        return
+    o, o_p = fast[0][:, :, pr], plain[0][:, :, pr]
+    lse, lse_p = fast[2][:, :, pr], plain[2][:, :, pr]
+    if desc.head_dim == 64:
+        assert torch.equal(o, o_p) and torch.equal(lse, lse_p), f"{label}: primal rows differ at d = 64"
+    else:
+        do = (o.float() - o_p.float()).abs().max().item()
+        dl = (lse - lse_p).abs().max().item()
+        print(f"[cmp] {label} primal rows: max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+        assert do <= 2e-2 * max(1.0, o_p.float().abs().max().item()), f"{label}: O on the primal rows"
+        assert dl <= 4e-3, f"{label}: lse on the primal rows"
 
 
 def _layout_desc(w):
@@ -47,7 +78,7 @@ def test_teacher_forcing_reduced_every_element(D, out_dtype):
     fast = aj.attn_jvp_mask_desc_tangent_free(base, [(0, w.seq_len // 2)])
     assert fast.work()[2] > 0 and fast.work()[1] > 0
     got = _run(dev, fast, out_dtype)
-    _same_as_plain(got, _run(dev, base, out_dtype), w.name)
+    _same_as_plain(got, _run(dev, base, out_dtype), w.name, fast)
     x = as_float64(inputs)
     ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], oracle_mask(w), scale=w.scale)
     res = compare(w, [to_np(t) for t in got], ref, label=w.name)
@@ -78,7 +109,7 @@ def test_rect_masks_with_tangent_free_ranges(case):
     base = aj.attn_jvp_mask_desc_from_rects(L, rects, head_dim=D, dtype="bf16")
     fast = aj.attn_jvp_mask_desc_tangent_free(base, ranges)
     got = _run(dev, fast)
-    _same_as_plain(got, _run(dev, base), "rects")
+    _same_as_plain(got, _run(dev, base), "rects", fast)
     x = as_float64(inputs)
     ref = attn_jvp_ref(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], RectMask(L, rects), scale=w.scale)
     compare(w, [to_np(t) for t in got], ref, label="rects")
@@ -93,7 +124,7 @@ def test_full_size_teacher_forcing_fast_path():
     fast = aj.attn_jvp_mask_desc_tangent_free(base, [(0, w.seq_len // 2)])
     got = _run(dev, fast)
     plain = _run(dev, base)
-    _same_as_plain(got, plain, w.name)
+    _same_as_plain(got, plain, w.name, fast)
     del plain
     o, to, lse = got
     assert (to[:, :, : w.seq_len // 2] == 0).all()
