@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libattnjvp.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["attn_jvp_fwd.hip", "attn_bwd.hip", "attn_jvp_api.cpp", "mask_desc.cpp"]
+SOURCES = ["attn_jvp_fwd.hip", "attn_fwd_q32.hip", "attn_bwd.hip", "attn_jvp_api.cpp", "mask_desc.cpp"]
 ARCH = os.environ.get("AJ_OFFLOAD_ARCH", "gfx950")
 
 

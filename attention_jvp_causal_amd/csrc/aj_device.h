@@ -184,4 +184,38 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Lazy rescale of the online softmax: a row's reference max moves only when
+// its max grows by more than 2^8 (log2 units).
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+// Key-tile buffers of the bf16 kernels: NT = 4 tensors (K, tK, V, tV) for the
+// JVP, NT = 2 (K, V) for the primal forward, whose smaller footprint lets two
+// workgroups share a CU.
+template <int D, int NT>
+struct Bf16Lds {
+  static constexpr int TILE = BN * D;  // elements per tensor tile
+  uint16_t t[2][NT][TILE];             // [buffer][tensor]
+  uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
+  // LDS slot of tensor t in {0: K, 1: tK, 2: V, 3: tV}
+  static constexpr __device__ int slot(int t) { return NT == 4 ? t : t / 2; }
+};
+// Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
+// when TANG, into one LDS buffer.  Returns immediately; completion is tracked
+// by vmcnt.  The buffer resource ends at row L, so rows past the end read as
+// zero.
+template <int NW, int D, bool TANG, int NT>
+__device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
+                                                 const uint16_t* const src[4], int64_t sl, int key0, int L,
+                                                 int wave) {
+  const int nrec = int((int64_t)min(L - key0, BN) * sl * 2);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (!TANG && (t & 1)) continue;  // tK, tV
+    const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
+#pragma unroll
+    for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
+      lds_dma_16(lds_addr(dst[NT == 4 ? t : t / 2] + (wave + NW * i) * 512), plan.voff[i], rs);
+  }
+}
+
 }  // namespace aj

@@ -69,6 +69,10 @@ inline int32_t head_group_for(int32_t BH) { return BH < kHeadGroup ? BH : kHeadG
 // Enqueues the dQ kernel and then the dK / dV kernel on `stream`.
 int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream);
 
+// Enqueues the 16-row JVP kernel at head_dim 128 (attn_jvp_fwd.hip); the
+// variants instance when the descriptor declares tangent-free tiles.
+void launch_q16(const FwdArgs& a, bool out_f32, bool variants, dim3 grid, hipStream_t stream);
+
 // Enqueues the forward kernel; returns an aj_status.  jvp = false computes
 // only O and lse (tq, tk, tv and to are not used).  variants = true when the
 // descriptor declares tangent-free tiles: the kernel instance that skips

@@ -31,7 +31,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cmath>
 #include <type_traits>
 
 #include "aj_device.h"
@@ -40,77 +39,33 @@
 
 namespace aj {
 
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr float kLazyRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2^8
-
 // ---------------------------------------------------------------------------
-// bf16 inputs
+// bf16 inputs, 16-row waves (the JVP at head_dim 128)
 // ---------------------------------------------------------------------------
 //
-// Two wave shapes share one streaming scheme; the launcher picks by head_dim.
+// A workgroup is 8 waves (two per SIMD); wave w owns query rows 16w .. 16w+15
+// of the 128-row tile.  With 16 rows per wave the row state (Q, tQ, O~, A+B,
+// scores) fits in 256 registers, so each SIMD runs two waves and the hardware
+// overlaps one wave's softmax and LDS latency with the other wave's MFMAs.
+// MFMA v_mfma_f32_16x16x32_bf16 on transposed scores S^T = K Q^T: lane
+// l = 16g + j holds keys 4g + r (r = 0..3) of each 16-key block for query row
+// j, i.e. one query per 16-lane column with its keys split over the four
+// groups g.  Two 16-key blocks form the 8 k-slots of a value MFMA's B
+// operand, so the score accumulators feed O~^T += V^T P~^T directly.
 //
-// * q16 (head_dim 128): a workgroup is 8 waves (two per SIMD); wave w owns
-//   query rows 16w .. 16w+15 of the 128-row tile.  With 16 rows per wave the
-//   row state (Q, tQ, O~, A+B, scores) fits in 256 registers, so each SIMD
-//   runs two waves and the hardware overlaps one wave's softmax and LDS
-//   latency with the other wave's MFMAs.  MFMA v_mfma_f32_16x16x32_bf16 on
-//   transposed scores S^T = K Q^T: lane l = 16g + j holds keys 4g + r
-//   (r = 0..3) of each 16-key block for query row j, i.e. one query per
-//   16-lane column with its keys split over the four groups g.  Two 16-key
-//   blocks form the 8 k-slots of a value MFMA's B operand, so the score
-//   accumulators feed O~^T += V^T P~^T directly.
-// * q32 (head_dim 64): a workgroup is 4 waves of 32 rows each, two
-//   workgroups per CU; MFMA v_mfma_f32_32x32x16_bf16 on S^T, lanes l and
-//   l+32 share one query row.  At d = 64 the softmax's vector work matches
-//   the matrix work per element, and the larger waves amortise the per-tile
-//   fixed costs better.
-//
-// Both stream key tiles of 64 keys (K, tK, V, tV rows and, for partial
-// tiles, the 128 per-row key bitmasks) by direct buffer -> LDS DMA into a
-// double buffer: tile t+1 loads while tile t computes.  V and tV are read with
+// Key tiles of 64 keys (K, tK, V, tV rows and, for partial tiles, the 128
+// per-row key bitmasks) stream by direct buffer -> LDS DMA into a double
+// buffer: tile t+1 loads while tile t computes.  V and tV are read with
 // gfx950's LDS transpose read.  Rows are unpadded; 16-byte chunk c of row r is
-// stored at position c ^ swz(r), chosen per shape so that the operand reads
-// are free of bank conflicts (swz_q16 / swz_q32 in aj_device.h; the q16
-// D = 128 swizzle serves both the row reads of K and the transpose reads of
-// V, so every tile of a q16 kernel shares one layout).
+// stored at position c ^ swz_q16(r) (aj_device.h), one layout that keeps both
+// the row reads of K and the transpose reads of V free of bank conflicts.
+// The 32-row kernels of attn_fwd_q32.hip use the same streaming scheme.
 
 constexpr int kWavesQ16 = 8;
-constexpr int kWavesQ32 = 4;
-
-// Key-tile buffers of the bf16 kernels: NT = 4 tensors (K, tK, V, tV) for the
-// JVP, NT = 2 (K, V) for the primal forward, whose smaller footprint lets two
-// workgroups share a CU.
-template <int D, int NT>
-struct Bf16Lds {
-  static constexpr int TILE = BN * D;  // elements per tensor tile
-  uint16_t t[2][NT][TILE];             // [buffer][tensor]
-  uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
-  // LDS slot of tensor t in {0: K, 1: tK, 2: V, 3: tV}
-  static constexpr __device__ int slot(int t) { return NT == 4 ? t : t / 2; }
-};
-// Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
-// when TANG, into one LDS buffer.  Returns immediately; completion is tracked
-// by vmcnt.  The buffer resource ends at row L, so rows past the end read as
-// zero.
-template <int NW, int D, bool TANG, int NT>
-__device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
-                                                 const uint16_t* const src[4], int64_t sl, int key0, int L,
-                                                 int wave) {
-  const int nrec = int((int64_t)min(L - key0, BN) * sl * 2);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (!TANG && (t & 1)) continue;  // tK, tV
-    const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
-#pragma unroll
-    for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-      lds_dma_16(lds_addr(dst[NT == 4 ? t : t / 2] + (wave + NW * i) * 512), plan.voff[i], rs);
-  }
-}
 
 // ---- q16 shape --------------------------------------------------------------
 
-template <int D, bool OUT_F32, bool JVP, bool VARIANTS>
+template <int D, bool OUT_F32, bool VARIANTS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ16, 64 * kWavesQ16), amdgpu_waves_per_eu(2, 2)))
 void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   constexpr int NKS = D / 32;  // MFMA k-steps over d for the score products
@@ -128,9 +83,9 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const int64_t kv_off = bb * a.ksb + hh * a.ksh;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
-  const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
-                                  (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
+  const uint16_t* __restrict__ tQg = (const uint16_t*)a.tq + in_off;
+  const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, (const uint16_t*)a.tk + kv_off,
+                                  (const uint16_t*)a.v + kv_off, (const uint16_t*)a.tv + kv_off};
   const int q_row = qt * BM + wave * 16 + j16;
 
   // Q and tQ of this lane's query row, as B operands: k-step ks holds
@@ -142,7 +97,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks) {
       const int64_t off = q_row * a.isl + ks * 32 + 8 * g;
       Qr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
-      tQr[ks] = as_bf16x8(JVP && q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
+      tQr[ks] = as_bf16x8(q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
     }
   }
   // Q and tQ have landed before any DMA is in flight: the compiler tracks no
@@ -152,7 +107,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   const TileLoadPlan<kWavesQ16, D> plan(a.ksl, wave, lane, swz_q16<D>);
   // DMA of key tile kti of entry x (tangent tiles only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
-    if (JVP && (!VARIANTS || x.flags == kTileJvp))
+    if (!VARIANTS || x.flags == kTileJvp)
       issue_tile_loads<kWavesQ16, D, true, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
       issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
@@ -203,8 +158,8 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   // One 64-key tile of the variant VAR (which tangents the tile carries).
   auto tile = [&](auto var_tag) __attribute__((always_inline)) {
     constexpr int VAR = decltype(var_tag)::value;
-    constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
-    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
+    constexpr bool HAS_TS = VAR != kTileAllFree;  // score tangent nonzero
+    constexpr bool HAS_TKV = VAR == kTileJvp;     // tK and tV tiles present
     const uint16_t* Kt = s.t[buf][0];
     const uint16_t* tKt = s.t[buf][1];
     const uint16_t* Vt = s.t[buf][2];
@@ -272,13 +227,11 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) Oacc[db][r] *= alpha;
-      if constexpr (JVP) {
-        mu_part *= alpha;
+      mu_part *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ABacc[db][r] *= alpha;
-      }
+        for (int r = 0; r < 4; ++r) ABacc[db][r] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
@@ -368,9 +321,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
-    if constexpr (!JVP) {
-      tile(std::integral_constant<int, kTileAllFree>{});
-    } else if constexpr (!VARIANTS) {
+    if constexpr (!VARIANTS) {
       tile(std::integral_constant<int, kTileJvp>{});
     } else {
       const int var = __builtin_amdgcn_readfirstlane(en.flags);
@@ -386,7 +337,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
 
   // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
   const float l_tot = row4_sum(l_part);
-  const float mu_tot = JVP ? row4_sum(mu_part) : 0.f;
+  const float mu_tot = row4_sum(mu_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // the lane's group, recomputed here rather than kept live across the loop
   const int ge = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) >> 4;
@@ -404,10 +355,10 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
       }
       if constexpr (OUT_F32) {
         *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
-        if constexpr (JVP) *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
+        *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
       } else {
         *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
-        if constexpr (JVP) *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
+        *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
       }
     }
     if (ge == 0)
@@ -415,529 +366,16 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   }
 }
 
-// ---- q32 shape --------------------------------------------------------------
-
-// SCALE_IN_Q: the scale is a power of two in (0, 1] and is folded into the Q
-// and tQ registers (exact: a power-of-two multiple of a bf16 value is a bf16
-// value, and every fp32 partial sum of the score products scales with it), so
-// the MFMAs deliver c s and c ts and u = p~ (c ts) takes one multiply less.
-// The results are bit for bit those of the unfolded kernel.
-template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32), amdgpu_waves_per_eu(2, 2)))
-void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
-  constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
-  constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
-  constexpr int NT = JVP ? 4 : 2;
-  using Lds = Bf16Lds<D, NT>;
-  __shared__ __attribute__((aligned(1024))) Lds s;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int BH = a.B * a.H;
-  const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
-  const int rank = tc.rank, bh = tc.bh;
-  const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.tasks[rank];
-  const int L = a.L;
-  const int64_t in_off = bb * a.isb + hh * a.ish;
-  const int64_t kv_off = bb * a.ksb + hh * a.ksh;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
-  const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
-  const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
-                                  (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
-  const int q_row = qt * BM + wave * 32 + l32;
-
-  const TileLoadPlan<kWavesQ32, D> plan(a.ksl, wave, lane, swz_q32<D>);
-  // At d = 64 the tangent-free variants are not built (three copies of the
-  // tile code do not fit the register budget of two workgroups per CU): every
-  // tile runs the general code, which is exact when the declared tangents are
-  // zero.
-  auto prefetch = [&](int b, const Entry& x, int kti) {
-    (void)x.flags;
-    if (JVP)
-      issue_tile_loads<kWavesQ32, D, true, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
-    else
-      issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
-  };
-
-  // first key tile in flight before the prologue
-  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
-  int e = e0, kt = 0;
-  Entry en = {0, 0, -1, 0};
-  if (e < e1) {
-    en = a.entries[e];
-    kt = en.kt0;
-    prefetch(0, en, kt);
-  }
-
-  // Q and tQ of this lane's query row, as B operands: k-step kk holds
-  // d = 16kk + 8hi .. 16kk + 8hi + 7.
-  bf16x8_t Qr[NKK], tQr[NKK];
-  {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int64_t off = q_row * a.isl + kk * 16 + 8 * hi;
-      Qr[kk] = as_bf16x8(q_row < L ? *(const u32x4_t*)(Qg + off) : zero);
-      tQr[kk] = as_bf16x8(JVP && q_row < L ? *(const u32x4_t*)(tQg + off) : zero);
-    }
-  }
-  // Q, tQ and the first key tile have landed; nothing the compiler tracks is
-  // in flight inside the loop below.
-  wait_vmcnt<0>();
-  if constexpr (SCALE_IN_Q) {
-    typedef float f32x8_t __attribute__((ext_vector_type(8)));
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      Qr[kk] = __builtin_convertvector(__builtin_convertvector(Qr[kk], f32x8_t) * a.scale, bf16x8_t);
-      tQr[kk] = __builtin_convertvector(__builtin_convertvector(tQr[kk], f32x8_t) * a.scale, bf16x8_t);
-    }
-  }
-
-  f32x16_t Oacc[NDB], ABacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
-  float m_run = -INFINITY;            // reference max (log2 units, scale folded in)
-  float l_part = 0.f, mu_part = 0.f;  // this lane's half of the row sums
-  // log2(e) and 1 when the scale is already in the scores
-  const float sl2 = SCALE_IN_Q ? 1.44269504088896340736f : a.scale_log2, c = SCALE_IN_Q ? 1.0f : a.scale;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  int koff[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * D + (((2 * kk + hi) ^ swz_q32<D>(l32)) << 3);
-  const int g = lane >> 4, j = lane & 15;
-  const int vrow0 = 4 * hi + (j >> 2);
-  const int vd0 = 16 * (g & 1) + 4 * (j & 3);
-  int voff[2][NDB];
-#pragma unroll
-  for (int h8 = 0; h8 < 2; ++h8)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int row = vrow0 + 8 * h8;
-      voff[h8][db] = row * D + (((4 * db + (vd0 >> 3)) ^ swz_q32<D>(row)) << 3) + (vd0 & 7);
-    }
-
-  int buf = 0;
-
-  // One 64-key tile of the variant VAR (which tangents the tile carries).
-  auto tile = [&](auto var_tag) __attribute__((always_inline)) {
-    constexpr int VAR = decltype(var_tag)::value;
-    constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
-    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
-    const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
-    const uint16_t* Kt = s.t[buf][Lds::slot(0)];
-    const uint16_t* tKt = s.t[buf][Lds::slot(1)];
-    const uint16_t* Vt = s.t[buf][Lds::slot(2)];
-    const uint16_t* tVt = s.t[buf][Lds::slot(3)];
-
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      // ---- scores and score tangents of 32 keys (transposed: lane = query) ----
-      f32x16_t S, TS;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = TS[r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int off = kb * 32 * D + koff[kk];
-        const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
-        bf16x8_t tkop;
-        if constexpr (HAS_TKV) tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
-        if constexpr (HAS_TKV) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
-        if constexpr (HAS_TS) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, tQr[kk], TS, 0, 0, 0);
-      }
-      // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
-
-      // ---- partial tile: masked-out pairs take no part (select; no tangent) ----
-      if (en.pidx >= 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = (bits >> key) & 1ull;
-          S[r] = ok ? S[r] : -INFINITY;
-          if constexpr (HAS_TS) TS[r] = ok ? TS[r] : 0.f;
-        }
-      }
-
-      // ---- online softmax with lazy rescale ----
-      float mx = S[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-      mx = row_max_halves(mx);
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const bool need = m_new > m_run + kLazyRescaleLog2;
-      if (__any(need)) {
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        m_run = need ? m_new : m_run;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) Oacc[db][r] *= alpha;
-        if constexpr (JVP) {
-          mu_part *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ABacc[db][r] *= alpha;
-        }
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-
-      // p~ = exp2(c log2e s - m); u = p~ * (c ts).  Both rounded to bf16 once;
-      // l and mu are summed from the rounded values.
-      bf16x8_t P[2], U[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const int r = 8 * st + t;
-          f32x2_t p, u;
-          p.x = fast_exp2(__builtin_fmaf(S[r], sl2, -m_use));
-          p.y = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -m_use));
-          if constexpr (HAS_TS) {
-            u.x = p.x * (TS[r] * c);
-            u.y = p.y * (TS[r + 1] * c);
-          }
-          const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
-          bf16x2_t ub;
-          if constexpr (HAS_TS) ub = __builtin_convertvector(u, bf16x2_t);
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
-          if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
-          P[st][t] = pb.x;
-          P[st][t + 1] = pb.y;
-          if constexpr (HAS_TS) {
-            U[st][t] = ub.x;
-            U[st][t + 1] = ub.y;
-          }
-        }
-
-      // ---- value products (transposed: rows = d, cols = queries) ----
-      //   O~ += V^T P~^T ;  (A + B) += V^T U^T + tV^T P~^T
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          // keys kb*32 + 16st + vrow0 (slots 0..3) and 8 further (slots 4..7)
-          const int off_a = (kb * 32 + 16 * st) * D + voff[0][db];
-          const int off_b = (kb * 32 + 16 * st) * D + voff[1][db];
-          const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
-          const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
-          s16x4_t ta, tb;
-          if constexpr (HAS_TKV) {
-            ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
-            tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
-          }
-          const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[st], Oacc[db], 0, 0, 0);
-          if constexpr (HAS_TS) ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, U[st], ABacc[db], 0, 0, 0);
-          if constexpr (HAS_TKV) {
-            const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
-            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tvop, P[st], ABacc[db], 0, 0, 0);
-          }
-        }
-      }
-    }
-  };
-
-  while (e < e1) {
-    // next key tile, loaded into the other buffer while this one is computed
-    int e_n = e, kt_n = kt + 1;
-    Entry en_n = en;
-    if (kt_n >= en.kt1) {
-      e_n = e + 1;
-      if (e_n < e1) {
-        en_n = a.entries[e_n];
-        kt_n = en_n.kt0;
-      }
-    }
-    // One barrier per tile: after it, every wave's loads of this tile have
-    // landed and every wave is done with the other buffer, which the next
-    // tile's DMA then refills.
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
-    if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{});
-    else tile(std::integral_constant<int, kTileJvp>{});
-    e = e_n;
-    kt = kt_n;
-    en = en_n;
-    buf ^= 1;
-  }
-
-  // ---- epilogue (Eq. 45): O = O~/l, tO = (A + B - mu O)/l ----
-  const float l_tot = l_part + wave_xor32(l_part);
-  const float mu_tot = JVP ? mu_part + wave_xor32(mu_part) : 0.f;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_row < L) {
-    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + 8 * gq + 4 * hi;
-        f32x4_t ov, tv;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 4 * gq + jj;
-          const float o = Oacc[db][r] * inv;
-          ov[jj] = o;
-          tv[jj] = (ABacc[db][r] - mu_tot * o) * inv;
-        }
-        if constexpr (OUT_F32) {
-          *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
-          if constexpr (JVP) *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
-        } else {
-          *(bf16x4_t*)((__bf16*)a.o + out_off + d0) = __builtin_convertvector(ov, bf16x4_t);
-          if constexpr (JVP) *(bf16x4_t*)((__bf16*)a.to + out_off + d0) = __builtin_convertvector(tv, bf16x4_t);
-        }
-        // primal rows of a JVP call (all their tangents declared zero): tO = 0
-        if constexpr (!JVP) {
-          if (a.to) {
-            if constexpr (OUT_F32) *(f32x4_t*)((float*)a.to + out_off + d0) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            else *(u32x2_t*)((__bf16*)a.to + out_off + d0) = u32x2_t{0u, 0u};
-          }
-        }
-      }
-    if (hi == 0)
-      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// fp32 inputs: same decomposition with MFMA 32x32x2 fp32 and no rounding of
-// p~ or p~.ts.  V needs no transpose: with two keys per MFMA step each lane
-// reads one value of a key row.
-// ---------------------------------------------------------------------------
-
-template <int D>
-struct F32Lds {
-  static constexpr int P = D + 4;
-  float k[BN * P];
-  float tk[BN * P];
-  float v[BN * P];
-  float tv[BN * P];
-};
-
-template <int D>
-__device__ __forceinline__ void stage_one_f32(float* __restrict__ dst, const float* __restrict__ src,
-                                              int64_t sl, int key0, int L, int tid) {
-  constexpr int CH = D / 4;  // 16-byte chunks per row
-  constexpr int N = BN * CH / NTHREADS;
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t r[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int c = tid + i * NTHREADS;
-    const int key = c / CH, col = (c % CH) * 4;
-    const int gk = key0 + key;
-    r[i] = gk < L ? *(const f32x4_t*)(src + gk * sl + col) : zero;
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int c = tid + i * NTHREADS;
-    const int key = c / CH, col = (c % CH) * 4;
-    *(f32x4_t*)(dst + key * F32Lds<D>::P + col) = r[i];
-  }
-}
-
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
-void attn_jvp_fwd_f32_kernel(FwdArgs a) {
-  constexpr int NKK = D / 2;
-  constexpr int NDB = D / 32;
-  using Lds = F32Lds<D>;
-  __shared__ __attribute__((aligned(16))) Lds s;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int BH = a.B * a.H;
-  const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
-  const int rank = tc.rank, bh = tc.bh;
-  const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.tasks[rank];
-  const int L = a.L;
-  const int64_t in_off = bb * a.isb + hh * a.ish;
-  const float* __restrict__ Qg = (const float*)a.q + in_off;
-  const int64_t kv_off = bb * a.ksb + hh * a.ksh;
-  const float* __restrict__ Kg = (const float*)a.k + kv_off;
-  const float* __restrict__ Vg = (const float*)a.v + kv_off;
-  const float* __restrict__ tQg = (const float*)a.tq + in_off;
-  const float* __restrict__ tKg = (const float*)a.tk + kv_off;
-  const float* __restrict__ tVg = (const float*)a.tv + kv_off;
-  const int q_row = qt * BM + wave * 32 + l32;
-
-  float Qr[NKK], tQr[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int64_t off = q_row * a.isl + 2 * kk + hi;
-    Qr[kk] = q_row < L ? Qg[off] : 0.f;
-    tQr[kk] = q_row < L ? tQg[off] : 0.f;
-  }
-
-  f32x16_t Oacc[NDB], ABacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Oacc[db][r] = ABacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_part = 0.f, mu_part = 0.f;
-  const float sl2 = a.scale_log2, c = a.scale;
-
-  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
-  for (int e = e0; e < e1; ++e) {
-    const Entry en = a.entries[e];
-    const uint64_t bits = en.pidx >= 0 ? a.bits[(int64_t)en.pidx * BM + wave * 32 + l32] : ~0ull;
-    for (int kt = en.kt0; kt < en.kt1; ++kt) {
-      __syncthreads();
-      stage_one_f32<D>(s.k, Kg, a.ksl, kt * BN, a.Lk, tid);
-      stage_one_f32<D>(s.tk, tKg, a.ksl, kt * BN, a.Lk, tid);
-      stage_one_f32<D>(s.v, Vg, a.ksl, kt * BN, a.Lk, tid);
-      stage_one_f32<D>(s.tv, tVg, a.ksl, kt * BN, a.Lk, tid);
-      __syncthreads();
-
-#pragma unroll 1
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        f32x16_t S, TS;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = TS[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int off = (kb * 32 + l32) * Lds::P + 2 * kk + hi;
-          const float kop = s.k[off], tkop = s.tk[off];
-          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, Qr[kk], S, 0, 0, 0);
-          TS = __builtin_amdgcn_mfma_f32_32x32x2f32(tkop, Qr[kk], TS, 0, 0, 0);
-          TS = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, tQr[kk], TS, 0, 0, 0);
-        }
-        if (en.pidx >= 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool ok = (bits >> key) & 1ull;
-            S[r] = ok ? S[r] : -INFINITY;
-            TS[r] = ok ? TS[r] : 0.f;
-          }
-        }
-        float mx = S[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const bool need = m_new > m_run + kLazyRescaleLog2;
-        if (__any(need)) {
-          const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-          m_run = need ? m_new : m_run;
-          l_part *= alpha;
-          mu_part *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              Oacc[db][r] *= alpha;
-              ABacc[db][r] *= alpha;
-            }
-        }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float P[16], U[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          P[r] = fast_exp2(__builtin_fmaf(S[r], sl2, -m_use));
-          U[r] = P[r] * (TS[r] * c);
-          l_part += P[r];
-          mu_part += U[r];
-        }
-        // two keys per MFMA step: lanes hi = 0 / 1 supply key 8*(r/4) + 4*hi + r%4
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int off = key * Lds::P + db * 32 + l32;
-            const float vop = s.v[off], tvop = s.tv[off];
-            Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, P[r], Oacc[db], 0, 0, 0);
-            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, U[r], ABacc[db], 0, 0, 0);
-            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(tvop, P[r], ABacc[db], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  const float l_tot = l_part + wave_xor32(l_part);
-  const float mu_tot = mu_part + wave_xor32(mu_part);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_row < L) {
-    const int64_t out_off = bb * a.osb + hh * a.osh + q_row * a.osl;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hi;
-        f32x4_t ov, tv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          const float o = Oacc[db][r] * inv;
-          ov[j] = o;
-          tv[j] = (ABacc[db][r] - mu_tot * o) * inv;
-        }
-        *(f32x4_t*)((float*)a.o + out_off + d0) = ov;
-        *(f32x4_t*)((float*)a.to + out_off + d0) = tv;
-      }
-    if (hi == 0)
-      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-
-template <bool JVP, bool VARIANTS>
-static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid, hipStream_t stream) {
-  const dim3 b16(64 * kWavesQ16), b32(64 * kWavesQ32);
-  if (!JVP && head_dim == 128) {
-    // primal forward: 32-row waves, two workgroups per CU
-    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, true, false>), grid, b32, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, false, false>), grid, b32, 0, stream, a);
-  } else if (head_dim == 128) {
-    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, JVP, VARIANTS>), grid, b16, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, JVP, VARIANTS>), grid, b16, 0, stream, a);
+// Enqueues the 16-row JVP kernel (head_dim 128) over `grid` workgroups.
+void launch_q16(const FwdArgs& a, bool out_f32, bool variants, dim3 grid, hipStream_t stream) {
+  const dim3 block(64 * kWavesQ16);
+  if (variants) {
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, true>), grid, block, 0, stream, a);
   } else {
-    // the JVP with a power-of-two scale (1/8 is the usual one at d = 64):
-    // the scale folded into Q and tQ
-    int e2 = 0;
-    const bool pow2 = a.scale > 0.f && a.scale <= 1.f && std::frexp(a.scale, &e2) == 0.5f;
-    if constexpr (JVP) {
-      if (pow2) {
-        if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true>), grid, b32, 0, stream, a);
-        else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, true>), grid, b32, 0, stream, a);
-        return;
-      }
-    }
-    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, JVP>), grid, b32, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, JVP>), grid, b32, 0, stream, a);
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q16_kernel<128, false, false>), grid, block, 0, stream, a);
   }
-}
-
-int launch_fwd(FwdArgs a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
-               hipStream_t stream) {
-  const int64_t grid64 = int64_t(a.n_tasks) * a.B * a.H;
-  if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
-  a.head_group = head_group_for(a.B * a.H);
-  const dim3 grid((unsigned)grid64);
-  if (in_dtype == AJ_BF16) {
-    if (!jvp) launch_bf16<false, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);
-    else if (variants) launch_bf16<true, true>(a, out_dtype == AJ_F32, head_dim, grid, stream);
-    else launch_bf16<true, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);
-  } else {
-    // fp32 inputs: the JVP only; tangent-free tiles run the general code
-    // (their tangents are zero, so every extra product adds zero)
-    if (!jvp) return AJ_ENOTSUP;
-    const dim3 b_f32(NTHREADS);
-    if (head_dim == 128) hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<128>), grid, b_f32, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_f32_kernel<64>), grid, b_f32, 0, stream, a);
-  }
-  return hipGetLastError() == hipSuccess ? AJ_OK : AJ_EHIP;
 }
 
 }  // namespace aj

@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -44,7 +45,9 @@ METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak,
 METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_BWD = "masked attention backward TFLOP/s (unmasked FLOPs, 10d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_KV = "KV-cache chunk attention TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
-KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n) for n in ("aj_device.h", "attn_jvp_fwd.hip")]
+# What the measured JVP kernel (16-row waves, head_dim 128) is built from.
+KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n)
+               for n in ("aj_internal.h", "aj_launch.h", "aj_device.h", "attn_jvp_fwd.hip")]
 
 
 def kernel_sha() -> str:
@@ -61,14 +64,27 @@ def kernel_sha() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def kernel_name(dtype: str, head_dim: int, out_f32: bool, jvp: bool = True, variants: bool = False) -> str:
-    """Name of the kernel instance the library launches for this configuration."""
+def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tangent_free: bool = False,
+                scale: float = None) -> str:
+    """Name of the kernel instance(s) the library launches for this call."""
+    b = lambda x: "true" if x else "false"
+    o = b(out_f32)
+    if op == "bwd":
+        return f"attn_bwd_dq32_kernel<{head_dim}, {o}> + attn_bwd_dkdv_kernel<{head_dim}, {o}>"
     if dtype == "f32":
         return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
-    b = lambda x: "true" if x else "false"
+    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false>"
+    if op in ("fwd", "kv"):
+        return primal
     if head_dim == 128:
-        return f"attn_jvp_fwd_bf16_q16_kernel<128, {b(out_f32)}, {b(jvp)}, {b(jvp and variants)}>"
-    return f"attn_jvp_fwd_bf16_q32_kernel<64, {b(out_f32)}, {b(jvp)}>"
+        jvp = f"attn_jvp_fwd_bf16_q16_kernel<128, {o}, {b(tangent_free)}>"
+    else:
+        s = 1.0 / math.sqrt(head_dim) if scale is None else scale
+        m, _ = math.frexp(s)
+        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}>"
+    # a tangent-free descriptor runs its primal-only query tiles through the
+    # primal kernel first
+    return f"{primal} + {jvp}" if tangent_free else jvp
 
 
 def measured_traffic(workload: str):
@@ -345,8 +361,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": (kernel_name(w.dtype, D, odt == torch.float32, args.op == "jvp", args.tangent_free)
-                       if args.op != "bwd" else "attn_bwd_dq32_kernel + attn_bwd_dkdv_kernel"),
+            "kernel": kernel_name(w.dtype, D, odt == torch.float32, args.op, args.tangent_free, w.scale),
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,
