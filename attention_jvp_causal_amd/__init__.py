@@ -278,6 +278,8 @@ def _prepare(ins, out_dtype, scale, out, n_out_tensors):
         *outs, lse = out
         if len(outs) != n_out_tensors:
             raise ValueError(f"out must hold {n_out_tensors + 1} tensors")
+        if any(t.device != x0.device for t in (*outs, lse)):
+            raise ValueError("preallocated outputs must be on the inputs' device")
         for o in outs:
             if o.shape != x0.shape or o.dtype != odt:
                 raise ValueError("preallocated outputs have the wrong shape or dtype")
@@ -365,6 +367,8 @@ def attn_fwd_kv(q, k_cache, v_cache, mask: MaskDesc, scale: Optional[float] = No
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        if o.device != q.device or lse.device != q.device:
+            raise ValueError("preallocated outputs must be on the inputs' device")
         if o.shape != q.shape or o.dtype != odt or o.stride(3) != 1:
             raise ValueError("preallocated o has the wrong shape, dtype or layout")
         if lse.shape != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():

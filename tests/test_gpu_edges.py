@@ -123,3 +123,20 @@ def test_head_groups_with_a_ragged_last_group(D):
         t = to_np(t)
         err = np.linalg.norm(t - r) / np.linalg.norm(r)
         assert err <= 1e-2, f"hgroups_{D} {name}: rel-L2 {err:.3e}"
+
+
+def test_binding_rejects_outputs_on_another_device():
+    # the C ABI sees plain pointers; the binding checks that preallocated
+    # outputs live on the inputs' device before passing them on
+    w = Workload("dev", 1, 1, 64, "bf16", "full", 1, 64, 1, seed=157)
+    dev = {n: t.cuda() for n, t in make_inputs(w).items()}
+    desc = aj.attn_jvp_mask_desc_build("full", 1, 64, 1, head_dim=64, dtype="bf16")
+    host = (torch.empty(w.shape, dtype=torch.bfloat16), torch.empty(w.shape, dtype=torch.bfloat16),
+            torch.empty((1, 1, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, out=host)
+    with pytest.raises(ValueError):
+        aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc, out=(host[0], host[2]))
+    kvd = aj.attn_jvp_mask_desc_from_rects_kv(64, 64, [(0, 64, 0, 64)], head_dim=64, dtype="bf16")
+    with pytest.raises(ValueError):
+        aj.attn_fwd_kv(dev["q"], dev["k"], dev["v"], kvd, out=(host[0], host[2]))
