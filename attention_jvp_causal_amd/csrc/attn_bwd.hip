@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "aj_device.h"
 #include "aj_internal.h"
 #include "aj_launch.h"
@@ -174,7 +176,8 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
     wait_vmcnt<0>();
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
-    const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
+    const bool part = en.pidx >= 0;  // uniform: only partial tiles test the row mask
+    const uint64_t bits = part ? s.bits[buf][wave * 32 + l32] : ~0ull;
     const uint16_t* Kt = s.t[buf][0];
     const uint16_t* Vt = s.t[buf][1];
 
@@ -194,22 +197,30 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
       }
       // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
       bf16x8_t DS[2];
+      auto make_ds = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const int r = 8 * st + t;
-          const int key0 = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok0 = (bits >> key0) & 1ull, ok1 = (bits >> (key0 + 1)) & 1ull;
-          const float p0 = fast_exp2(__builtin_fmaf(S[r], sl2, -lse_l2));
-          const float p1 = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -lse_l2));
-          f32x2_t ds;
-          ds.x = ok0 ? p0 * (dP[r] - delta) : 0.f;
-          ds.y = ok1 ? p1 * (dP[r + 1] - delta) : 0.f;
-          const bf16x2_t d2 = __builtin_convertvector(ds, bf16x2_t);
-          DS[st][t] = d2.x;
-          DS[st][t + 1] = d2.y;
-        }
+          for (int t = 0; t < 8; t += 2) {
+            const int r = 8 * st + t;
+            const float p0 = fast_exp2(__builtin_fmaf(S[r], sl2, -lse_l2));
+            const float p1 = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -lse_l2));
+            f32x2_t ds;
+            ds.x = p0 * (dP[r] - delta);
+            ds.y = p1 * (dP[r + 1] - delta);
+            if constexpr (MASKED) {
+              const int key0 = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              ds.x = (bits >> key0) & 1ull ? ds.x : 0.f;
+              ds.y = (bits >> (key0 + 1)) & 1ull ? ds.y : 0.f;
+            }
+            const bf16x2_t d2 = __builtin_convertvector(ds, bf16x2_t);
+            DS[st][t] = d2.x;
+            DS[st][t + 1] = d2.y;
+          }
+      };
+      if (part) make_ds(std::true_type{});
+      else make_ds(std::false_type{});
       // dQ^T += K^T dS^T (rows = d, columns = queries)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -368,32 +379,38 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop[qb], Vr[ks], dP[qb], 0, 0, 0);
     }
 
-    uint64_t bits = ~0ull;
-    if (en.pidx >= 0) bits = s.bits[buf][wave * 16 + j16] >> (4 * g);
+    const bool part = en.pidx >= 0;  // uniform: only partial tiles test the row mask
+    const uint64_t bits = part ? s.bits[buf][wave * 16 + j16] >> (4 * g) : ~0ull;
     bf16x8_t P[2], DS[2];
+    auto make_p_ds = [&](auto masked_tag) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][16 * qb + 4 * g]);
-      const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][16 * qb + 4 * g]);
+      for (int qb = 0; qb < 4; ++qb) {
+        const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][16 * qb + 4 * g]);
+        const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][16 * qb + 4 * g]);
 #pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const bool ok0 = (bits >> (16 * qb + r)) & 1ull, ok1 = (bits >> (16 * qb + r + 1)) & 1ull;
-        const float p0 = fast_exp2(__builtin_fmaf(S[qb][r], sl2, -lse4[r] * kLog2e));
-        const float p1 = fast_exp2(__builtin_fmaf(S[qb][r + 1], sl2, -lse4[r + 1] * kLog2e));
-        f32x2_t pv, ds;
-        pv.x = ok0 ? p0 : 0.f;
-        pv.y = ok1 ? p1 : 0.f;
-        ds.x = pv.x * (dP[qb][r] - del4[r]);
-        ds.y = pv.y * (dP[qb][r + 1] - del4[r + 1]);
-        const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
-        const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
-        const int slot = 4 * (qb & 1) + r;
-        P[qb >> 1][slot] = pb.x;
-        P[qb >> 1][slot + 1] = pb.y;
-        DS[qb >> 1][slot] = db2.x;
-        DS[qb >> 1][slot + 1] = db2.y;
+        for (int r = 0; r < 4; r += 2) {
+          f32x2_t pv, ds;
+          pv.x = fast_exp2(__builtin_fmaf(S[qb][r], sl2, -lse4[r] * kLog2e));
+          pv.y = fast_exp2(__builtin_fmaf(S[qb][r + 1], sl2, -lse4[r + 1] * kLog2e));
+          if constexpr (MASKED) {
+            pv.x = (bits >> (16 * qb + r)) & 1ull ? pv.x : 0.f;
+            pv.y = (bits >> (16 * qb + r + 1)) & 1ull ? pv.y : 0.f;
+          }
+          ds.x = pv.x * (dP[qb][r] - del4[r]);
+          ds.y = pv.y * (dP[qb][r + 1] - del4[r + 1]);
+          const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
+          const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
+          const int slot = 4 * (qb & 1) + r;
+          P[qb >> 1][slot] = pb.x;
+          P[qb >> 1][slot + 1] = pb.y;
+          DS[qb >> 1][slot] = db2.x;
+          DS[qb >> 1][slot + 1] = db2.y;
+        }
       }
-    }
+    };
+    if (part) make_p_ds(std::true_type{});
+    else make_p_ds(std::false_type{});
 
     // dV^T += dO^T P and dK^T += Q^T dS (rows = d, columns = keys)
 #pragma unroll
