@@ -26,7 +26,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def compile_flags():
+# Per-source scheduler choice. The gradient kernels run 1-2.5 % faster under
+# LLVM's iterative ILP scheduler than under the default (same-box A/B, both head
+# dims) and still spill nothing. The 32-row forward kernels gain about as much but
+# spill under it, and the 16-row JVP kernel gains nothing: both keep the default.
+SOURCE_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
+def compile_flags(src: str | None = None):
+    """hipcc flags shared by every source, plus the per-source ones for `src`."""
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: plain float code only
@@ -39,6 +49,7 @@ def compile_flags():
         # with VALU ops, which cannot address AGPRs
         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         f"-I{os.path.join(ROOT, 'include')}",
+        *SOURCE_FLAGS.get(src, []),
     ]
 
 
@@ -51,7 +62,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *compile_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(src), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,7 +17,7 @@ def _device_asm(tmp_path):
     text = []
     for src in (x for x in B.SOURCES if x.endswith(".hip")):
         out = tmp_path / (src + ".s")
-        cmd = [B.hipcc(), *B.compile_flags(), "-x", "hip", "-S", "--cuda-device-only",
+        cmd = [B.hipcc(), *B.compile_flags(src), "-x", "hip", "-S", "--cuda-device-only",
                os.path.join(B.CSRC, src), "-o", str(out)]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
