@@ -83,8 +83,11 @@ __device__ __forceinline__ float bf16_dot8(bf16x8_t x, bf16x8_t y, float acc) {
 // query tile and two workgroups share a CU.  Lanes l and l + 32 hold the same
 // query row; S^T, dP^T and dS^T keep the forward q32 kernel's layout, so the
 // K^T transpose reads and the slot order of the B operand are the same.
+// Two workgroups per CU at d = 128; three at d = 64 (at most 168 VGPRs, 34 KB
+// of LDS each).
 template <int D, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqWaves32), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqWaves32),
+                          amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void attn_bwd_dq32_kernel(BwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for S^T and dP^T
   constexpr int NDB = D / 32;  // 32-row blocks of d for dQ^T

@@ -42,8 +42,16 @@ constexpr int kWavesQ32 = 4;
 // value, and every fp32 partial sum of the score products scales with it), so
 // the MFMAs deliver c s and c ts and u = p~ (c ts) takes one multiply less.
 // The results are bit for bit those of the unfolded kernel.
+//
+// Occupancy: two workgroups per CU (two waves per SIMD, up to 256 VGPRs),
+// except the d = 64 primal kernel, which fits 168 VGPRs and 34 KB of LDS and
+// runs three.
+template <int D, bool JVP>
+constexpr int q32_waves_per_simd() { return D == 64 && !JVP ? 3 : 2; }
+
 template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32),
+                          amdgpu_waves_per_eu(q32_waves_per_simd<D, JVP>(), q32_waves_per_simd<D, JVP>())))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
