@@ -22,8 +22,10 @@
 //   lane column, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly,
 //   dO^T and Q^T coming from transpose reads.
 // dQ runs 4 waves of 32 rows (v_mfma_f32_32x32x16_bf16, two workgroups per
-// CU), dK / dV 8 waves of 16 keys (v_mfma_f32_16x16x32_bf16, two waves per
-// SIMD); both use the direct buffer -> LDS DMA into a double buffer and the
+// CU at d = 128, three at d = 64), dK / dV waves of 16 keys
+// (v_mfma_f32_16x16x32_bf16; 8 per workgroup and two waves per SIMD at
+// d = 128, 4 per workgroup and three per SIMD at d = 64); both use the direct
+// buffer -> LDS DMA into a double buffer and the
 // swizzled tile layouts of the forward kernels.  Masked pairs are removed by select
 // (P = dS = 0), never by arithmetic on -inf.
 #include <hip/hip_runtime.h>
@@ -37,7 +39,6 @@
 
 namespace aj {
 
-constexpr int kBwdWaves = 8;    // 16-row waves
 constexpr int kDqWaves32 = 4;   // 32-row waves of the dQ kernel
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -46,7 +47,7 @@ struct BwdLds {
   static constexpr int TILE = BN * D;  // elements per tensor tile
   uint16_t t[2][2][TILE];              // [buffer][(K, V) for dQ | (Q, dO) for dK, dV]
   uint64_t bits[2][BM];                // per-row bitmask of a partial tile
-  float rowv[2][2][256];               // [buffer][lse, D] of the 64 streamed queries
+  float rowv[2][2][BN];                // [buffer][lse, D] of the 64 streamed queries
 };
 
 // K and V tiles only (the 32-row dQ kernel): 66 KB, two workgroups per CU.
@@ -264,25 +265,35 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
 
 // ---- dK, dV -------------------------------------------------------------------
 
+// Waves of 16 keys per workgroup: 8 (one 128-key tile of the column map, two
+// waves per SIMD) at d = 128; 4 at d = 64, where the kernel fits 168 VGPRs and
+// three 64-key workgroups share a CU, each taking half of a column-map tile.
+template <int D>
+constexpr int dkdv_waves() { return D == 64 ? 4 : 8; }
+
 template <int D, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kBwdWaves, 64 * kBwdWaves), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * dkdv_waves<D>(), 64 * dkdv_waves<D>()),
+                          amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
+  constexpr int NW = dkdv_waves<D>();
+  constexpr int PARTS = BM / (16 * NW);  // workgroups per column-map tile
   __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
   const int BH = a.B * a.H;
-  const TaskCoord tc = task_coord(blockIdx.x, a.n_col_tasks, BH, a.head_group);
-  const int rank = tc.rank, bh = tc.bh;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_col_tasks * PARTS, BH, a.head_group);
+  const int rank = tc.rank / PARTS, kpart = tc.rank - rank * PARTS, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int ktile = a.cols.tasks[rank];
+  const int key_in_tile = kpart * 16 * NW + wave * 16 + j16;  // row of the tile's bitmask
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const int64_t bhL = (int64_t)bh * L;
   const uint16_t* Qg = (const uint16_t*)a.q + in_off;
   const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
-  const int k_row = ktile * BM + wave * 16 + j16;
+  const int k_row = ktile * BM + key_in_tile;
 
   // K, V of this lane's key as B operands (k-step ks: d = 32ks + 8g ..)
   bf16x8_t Kr[NKS], Vr[NKS];
@@ -299,12 +310,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vmcnt<0>();
 
-  const TileLoadPlan<kBwdWaves, D> plan(a.isl, wave, lane, swz_q16<D>);
+  const TileLoadPlan<NW, D> plan(a.isl, wave, lane, swz_q16<D>);
   // Q, dO rows of query tile qti; wave 1 brings their lse and D, wave 0 the
   // key bitmasks of a partial tile
   auto prefetch = [&](int b, const Entry& x, int qti) {
     const int row0 = qti * BN;
-    issue_pair_loads<kBwdWaves, D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
+    issue_pair_loads<NW, D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
     if (wave == 1) {
       const int nrec = min(L - row0, BN) * 4;
       lds_dma_4(lds_addr(s.rowv[b][0]), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
@@ -383,7 +394,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 
     const bool part = en.pidx >= 0;  // uniform: only partial tiles test the row mask
-    const uint64_t bits = part ? s.bits[buf][wave * 16 + j16] >> (4 * g) : ~0ull;
+    const uint64_t bits = part ? s.bits[buf][key_in_tile] >> (4 * g) : ~0ull;
     bf16x8_t P[2], DS[2];
     auto make_p_ds = [&](auto masked_tag) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
@@ -474,15 +485,17 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
 template <int D, bool OUT_F32>
 static void launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  const dim3 block(64 * kBwdWaves);
+  constexpr int NW = dkdv_waves<D>();
   hipLaunchKernelGGL((attn_bwd_dq32_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_row_tasks) * a.B * a.H)),
                      dim3(64 * kDqWaves32), 0, stream, a);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_col_tasks) * a.B * a.H)), block, 0,
-                     stream, a);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>),
+                     dim3(unsigned(int64_t(a.n_col_tasks) * (BM / (16 * NW)) * a.B * a.H)), dim3(64 * NW), 0, stream,
+                     a);
 }
 
 int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream) {
-  const int64_t g1 = int64_t(a.n_row_tasks) * a.B * a.H, g2 = int64_t(a.n_col_tasks) * a.B * a.H;
+  const int64_t parts = head_dim == 64 ? BM / (16 * dkdv_waves<64>()) : BM / (16 * dkdv_waves<128>());
+  const int64_t g1 = int64_t(a.n_row_tasks) * a.B * a.H, g2 = int64_t(a.n_col_tasks) * parts * a.B * a.H;
   if (g1 <= 0 || g2 <= 0 || g1 > 0x7fffffff || g2 > 0x7fffffff) return AJ_EINVAL;
   a.head_group = head_group_for(a.B * a.H);
   const bool f32 = out_dtype == AJ_F32;
