@@ -50,7 +50,8 @@ struct BwdLds {
   float rowv[2][2][BN];                // [buffer][lse, D] of the 64 streamed queries
 };
 
-// K and V tiles only (the 32-row dQ kernel): 66 KB, two workgroups per CU.
+// K and V tiles only (the 32-row dQ kernel): 66 KB at d = 128 (two workgroups
+// per CU), 34 KB at d = 64 (three).
 template <int D>
 struct KvLds {
   uint16_t t[2][2][BN * D];  // [buffer][K, V]

@@ -25,7 +25,8 @@ constexpr int NTHREADS = 64 * NWAVES;
 // bf16 inputs, 32-row waves
 // ---------------------------------------------------------------------------
 //
-// A workgroup is 4 waves of 32 rows each, two workgroups per CU; MFMA
+// A workgroup is 4 waves of 32 rows each, two workgroups per CU (three for the
+// d = 64 primal kernel); MFMA
 // v_mfma_f32_32x32x16_bf16 on S^T, lanes l and l+32 share one query row.  At
 // d = 64 the softmax's vector work matches the matrix work per element, and
 // the larger waves amortise the per-tile fixed costs better; without the
