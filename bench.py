@@ -31,6 +31,7 @@ import json
 import math
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -153,6 +154,74 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int
     return rec
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (the starred level of
+    pp_dpm_sclk) and board power (hwmon power1_input or power1_average) from
+    sysfs on a thread while the step repeats.  Read-only; the first DRM card
+    that exposes the clock is taken (one GPU per process here).  Under the MFMA
+    load of these kernels the chip runs below its 2.4 GHz peak, by an amount
+    that differs between boards: the clock explains most of the spread of
+    results across machines."""
+
+    def __init__(self, period_s: float = 0.02):
+        import glob
+
+        self.period = period_s
+        self.sclk = self.power = None
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(dev + "/pp_dpm_sclk"):
+                self.sclk = dev + "/pp_dpm_sclk"
+                pw = sorted(glob.glob(dev + "/hwmon/hwmon*/power1_input") +
+                            glob.glob(dev + "/hwmon/hwmon*/power1_average"))
+                self.power = pw[0] if pw else None
+                break
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        mhz = watts = None
+        try:
+            for line in open(self.sclk).read().splitlines():
+                if line.rstrip().endswith("*"):
+                    mhz = int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        try:
+            if self.power:
+                watts = int(open(self.power).read()) / 1e6
+        except (OSError, ValueError):
+            pass
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append(self._read())
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.sclk:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if not self._thread:
+            return None
+        self._stop.set()
+        self._thread.join()
+        med = lambda v: sorted(v)[len(v) // 2] if v else None
+        mhz = [m for m, _ in self.samples if m is not None]
+        watts = [w for _, w in self.samples if w is not None]
+        return {"sclk_mhz_median": med(mhz), "sclk_mhz_min": min(mhz) if mhz else None,
+                "board_power_w_median": med(watts), "samples": len(self.samples),
+                "source": "sysfs pp_dpm_sclk and hwmon power, sampled every 20 ms while the step repeats "
+                          "after the timed region"}
+
+
+def avg_ms_of(ev) -> float:
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+
+
 def cpu_baseline(w, inputs, heads: int):
     """Times the fp64 oracle (as it stands) on the first `heads` heads of batch 0."""
     import numpy as np
@@ -195,6 +264,9 @@ def main(argv=None):
                          "kv: last chunk over a KV cache")
     ap.add_argument("--tangent-free", action="store_true",
                     help="declare the clean half of a teacher-forcing workload tangent-free")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="seconds of repeated steps after the timed ones, sampling the shader clock and board "
+                         "power from sysfs (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -207,7 +279,8 @@ def main(argv=None):
 
         wl = args.workload or BENCH_WORKLOAD
         cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
-               f"--workload {wl} --steps 3 --warmup 1 --cpu-heads 0 --calib-copy-mib {args.calib_copy_mib or 1024}")
+               f"--workload {wl} --steps 3 --warmup 1 --cpu-heads 0 --clock-seconds 0 "
+               f"--calib-copy-mib {args.calib_copy_mib or 1024}")
         print(json.dumps(record_traffic(wl, *args.record_traffic, args.calib_copy_mib or 1024, cmd)))
         return 0
 
@@ -302,6 +375,23 @@ def main(argv=None):
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # Shader clock and board power under sustained load of the same step
+    # (about 2 s after the timed steps, outside them: the clock settles over
+    # a few hundred milliseconds, longer than the timed region).
+    gpu_clock = None
+    clock = ClockSampler()
+    if clock.sclk and args.clock_seconds > 0:
+        n_sus = max(1, int(args.clock_seconds * 1e3 / max(avg_ms_of(ev), 1e-3)))
+        clock.start()
+        for i in range(n_sus):
+            step()
+            if i % 8 == 7:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        gpu_clock = clock.stop()
+        if gpu_clock:
+            gpu_clock["steps"] = n_sus
     launch_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     avg_ms = sum(launch_ms) / len(launch_ms)
     ms_per_step = wall * 1e3 / args.steps
@@ -367,6 +457,7 @@ def main(argv=None):
             "algorithmic_hbm_bytes": in_bytes + out_bytes,
         },
         "cpu_baseline": cpu,
+        "gpu_clock": gpu_clock,
     }
     print(json.dumps(rec), flush=True)
     return 0
