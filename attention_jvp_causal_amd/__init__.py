@@ -191,6 +191,17 @@ class MaskDesc:
             pass
 
 
+def _flatten(items, width: int, what: str):
+    """Flattens a sequence of width-tuples of ints, rejecting tuples of any other length."""
+    flat = []
+    for r in items:
+        r = [int(x) for x in r]
+        if len(r) != width:
+            raise ValueError(f"each {what} needs {width} integers, got {len(r)}")
+        flat.extend(r)
+    return flat
+
+
 def attn_jvp_mask_desc_build(kind: str, num_frames: int, frame_tokens: int, frames_per_chunk: int = 1,
                              head_dim: int = 128, dtype="bf16", seq_len: Optional[int] = None) -> MaskDesc:
     """Descriptor for a frame-level layout (see ``aj_mask_kind`` in the header)."""
@@ -208,7 +219,7 @@ def attn_jvp_mask_desc_build(kind: str, num_frames: int, frame_tokens: int, fram
 def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], head_dim: int = 128,
                                   dtype="bf16") -> MaskDesc:
     """Descriptor from disjoint half-open rectangles (q0, q1, k0, k1)."""
-    flat = [int(x) for r in rects for x in r]
+    flat = _flatten(rects, 4, "rectangle")
     arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     out = ctypes.c_void_p()
     dt = _dtype_code(dtype)
@@ -222,7 +233,7 @@ def attn_jvp_mask_desc_from_rects_kv(q_len: int, kv_len: int, rects: Sequence[Se
                                      dtype="bf16") -> MaskDesc:
     """Descriptor for a query chunk of q_len tokens over kv_len cached keys, from
     disjoint half-open rectangles (q0, q1, k0, k1)."""
-    flat = [int(x) for r in rects for x in r]
+    flat = _flatten(rects, 4, "rectangle")
     arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     out = ctypes.c_void_p()
     dt = _dtype_code(dtype)
@@ -235,7 +246,7 @@ def attn_jvp_mask_desc_from_rects_kv(q_len: int, kv_len: int, rects: Sequence[Se
 def attn_jvp_mask_desc_tangent_free(base: MaskDesc, ranges: Sequence[Sequence[int]]) -> MaskDesc:
     """Descriptor with base's mask that declares tq, tk, tv zero on the token
     ranges [t0, t1) (see the header); the JVP then skips the zero products."""
-    flat = [int(x) for r in ranges for x in r]
+    flat = _flatten(ranges, 2, "range")
     arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     out = ctypes.c_void_p()
     _check(lib().attn_jvp_mask_desc_tangent_free(base.handle, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 2,

@@ -86,6 +86,18 @@ def test_from_rects_errors():
     assert aj.lib().attn_jvp_mask_desc_from_rects(100, None, 3, 128, aj.AJ_BF16, ctypes.byref(ctypes.c_void_p())) == aj.AJ_EINVAL
 
 
+def test_binding_rejects_ragged_rectangles_and_ranges():
+    with pytest.raises(ValueError):
+        aj.attn_jvp_mask_desc_from_rects(100, [(0, 50, 0)], head_dim=128)
+    with pytest.raises(ValueError):
+        aj.attn_jvp_mask_desc_from_rects_kv(10, 100, [(0, 10, 0, 100, 7)], head_dim=128)
+    base = aj.attn_jvp_mask_desc_build("block_causal", 4, 50, 1, head_dim=128)
+    with pytest.raises(ValueError):
+        aj.attn_jvp_mask_desc_tangent_free(base, [(0, 50, 60)])
+    d = aj.attn_jvp_mask_desc_tangent_free(base, [(0, 50)])
+    assert d.seq_len == 200
+
+
 def test_query_errors():
     lib = aj.lib()
     d = aj.attn_jvp_mask_desc_build("block_causal", 4, 50, 1, head_dim=128)
