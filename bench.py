@@ -53,8 +53,12 @@ KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n)
 
 def kernel_sha() -> str:
     """Hash of the JVP kernel's sources with comments and blank lines removed,
-    so that a counter record stays valid across comment-only edits."""
+    and of the compiler flags they are built with (include paths aside), so
+    that a counter record stays valid across comment-only edits and no
+    longer."""
     import re
+
+    from attention_jvp_causal_amd import build as _build
 
     src = ""
     for path in KERNEL_SRCS:
@@ -62,7 +66,8 @@ def kernel_sha() -> str:
             src += f.read()
     src = re.sub(r"//[^\n]*", "", src)
     code = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    flags = " ".join(f for f in _build.compile_flags("attn_jvp_fwd.hip") if not f.startswith("-I"))
+    return hashlib.sha256((code + "\n" + flags).encode()).hexdigest()[:16]
 
 
 def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tangent_free: bool = False,
