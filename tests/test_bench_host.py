@@ -51,3 +51,17 @@ def test_clock_sampler_without_sysfs_reports_nothing():
     c.sclk = c.power = None
     c.start()
     assert c.stop() is None
+
+
+def test_traffic_record_matches_the_kernel_sources():
+    # bench.py reports roofline.traffic only while the counter record was
+    # taken on the current kernel sources and flags; a kernel change needs a
+    # new record (bench.py --record-traffic)
+    from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{BENCH_WORKLOAD}.json")
+    with open(path) as f:
+        rec = json.load(f)
+    assert rec["kernel_sha"] == bench.kernel_sha()
+    assert rec["kernel"] == bench.kernel_name("bf16", 128, False)
+    assert bench.measured_traffic(BENCH_WORKLOAD) == rec["bytes_per_launch"] > 0
