@@ -1,7 +1,8 @@
 """The launch paths under HIP graph capture.
 
-After a first call (which uploads the descriptor's tables), attn_jvp_fwd,
-attn_fwd and attn_bwd enqueue kernels only: no allocation, no memset, no host
+After a first call (which uploads the descriptor's tables), attn_jvp_fwd (also
+with a tangent-free descriptor: two launches), attn_fwd, attn_fwd_kv and
+attn_bwd enqueue kernels only: no allocation, no memset, no host
 synchronisation.  They are captured into a graph on torch's capture stream and
 the graph is replayed several times, with eager work and synchronisation in
 between; every replay must reproduce the eager results bit for bit (the
@@ -61,4 +62,53 @@ def test_jvp_and_gradients_replay_from_a_graph():
         graph.replay()
         torch.cuda.synchronize()
         for got, ref in zip(jvp_out + fwd_out + bwd_out, want):
+            assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
+
+
+def test_tangent_free_path_and_kv_forward_replay_from_a_graph():
+    # the tangent-free descriptor takes two launches per call (primal-only
+    # query tiles, then the rest); the KV-cache forward reads a cache longer
+    # than the prefix it uses
+    w = Workload("graph_tf", 1, 2, 128, "bf16", "tf_clean_noisy", 4, 90, 1, seed=161, clean_tangent_zero=True)
+    dev = {n: t.cuda() for n, t in make_inputs(w).items()}
+    base = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    fast = aj.attn_jvp_mask_desc_tangent_free(base, [(0, w.seq_len // 2)])
+    assert fast.work()[2] > 0
+    B, H, L, D = w.shape
+    q_len, kv_len = 120, 300
+    kv_desc = aj.attn_jvp_mask_desc_from_rects_kv(q_len, kv_len, [(0, q_len, 0, kv_len)], head_dim=D, dtype="bf16")
+    q_chunk = dev["q"][:, :, L - q_len:]
+    jvp_out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    kv_out = (torch.empty((B, H, q_len, D), dtype=torch.bfloat16, device="cuda"),
+              torch.empty((B, H, q_len), dtype=torch.float32, device="cuda"))
+
+    def run():
+        aj.attn_jvp_fwd(*(dev[n] for n in NAMES), fast, scale=w.scale, out=jvp_out)
+        aj.attn_fwd_kv(q_chunk, dev["k"], dev["v"], kv_desc, scale=w.scale, out=kv_out)
+
+    run()  # eager; uploads the tables
+    torch.cuda.synchronize()
+    want = [t.clone() for t in jvp_out + kv_out]
+    assert bool((want[1][:, :, : L // 2] == 0).all())  # tO on the declared tangent-free rows
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for t in jvp_out + kv_out:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in jvp_out + kv_out:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(jvp_out + kv_out, want):
             assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
