@@ -132,3 +132,41 @@ def test_full_size_sampled(wname):
         _check("dq", to_np(dq[b, h, rows]), sq[(b, h)], f"{wname} b{b}h{h}")
         _check("dk", to_np(dk[b, h, keys]), sk[(b, h)], f"{wname} b{b}h{h}")
         _check("dv", to_np(dv[b, h, keys]), sv[(b, h)], f"{wname} b{b}h{h}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_strided_layout(D):
+    # inputs stored [B, L, H, D] and viewed as [B, H, L, D] (the five inputs
+    # share those strides); outputs in a permuted layout of their own
+    w = Workload("bwd_strided", 2, 3, D, "bf16", "block_causal", 4, 75, 2, seed=100 + D)
+    print(f"[case] bwd strided D={D}", flush=True)
+    inputs = make_inputs(w)
+    B, H, L, _ = w.shape
+    desc = _layout_desc(w)
+
+    def blhd(t):  # same values, [B, L, H, D] storage
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    q, k, v = (blhd(inputs[n]).cuda() for n in ("q", "k", "v"))
+    assert q.stride() != inputs["q"].stride()
+    o, lse = aj.attn_fwd(q, k, v, desc, scale=w.scale)
+    o_s = blhd(o.cpu()).cuda()
+    dO = _cotangent(w, 101)
+    dO_s = blhd(dO).cuda()
+    outs = tuple(torch.empty((B, L, H, D), dtype=torch.float32, device="cuda").permute(0, 2, 1, 3)
+                 for _ in range(3)) + (torch.empty((B, H, L), dtype=torch.float32, device="cuda"),)
+    dq, dk, dv, _ = aj.attn_bwd(q, k, v, o_s, dO_s, lse, desc, scale=w.scale, out_dtype=torch.float32, out=outs)
+    torch.cuda.synchronize()
+    # the same call on contiguous tensors gives the same bits
+    c = {n: inputs[n].cuda() for n in ("q", "k", "v")}
+    o_c, lse_c = aj.attn_fwd(c["q"], c["k"], c["v"], desc, scale=w.scale)
+    assert torch.equal(o_c, o) and torch.equal(lse_c, lse)
+    dq_c, dk_c, dv_c, _ = aj.attn_bwd(c["q"], c["k"], c["v"], o_c, dO.cuda(), lse_c, desc, scale=w.scale,
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for name, a, b in (("dq", dq, dq_c), ("dk", dk, dk_c), ("dv", dv, dv_c)):
+        assert torch.equal(a, b), f"strided {name} differs from the contiguous call"
+    x = {n: t.to(torch.float64).numpy() for n, t in inputs.items()}
+    ref = attn_vjp_ref(x["q"], x["k"], x["v"], dO.to(torch.float64).numpy(), oracle_mask(w), scale=w.scale)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        _check(name, to_np(g), r, f"strided d{D}")
