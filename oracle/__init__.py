@@ -13,8 +13,8 @@ the attention tangent written as sums over valid keys (Eq. 44).  The mask
 layouts follow Sec. 2.3 / Sec. 3.1.1 (teacher forcing, Eq. 8) and the chunk
 patterns c1-1 / c3-3 of Sec. 5.
 
-Pins (tests/test_oracle.py, tests/test_masks.py): central finite differences of
-the oracle's own primal, forward-mode autodiff of a dense masked attention,
+Pins (tests/test_oracle.py, tests/test_oracle_masks.py, tests/test_oracle_kv.py):
+central finite differences of the oracle's own primal, forward-mode autodiff of a dense masked attention,
 PyTorch's scaled_dot_product_attention and scipy's logsumexp as library special
 cases, per-element brute force on tiny inputs, the invariants of the JVP
 (linearity, zero tangents, tQ = tK = 0, masked-key perturbation, constant
@@ -25,10 +25,10 @@ identity with the (separately pinned) JVP, by central finite differences and by
 their sum rules.  Every function here is pinned; none is "parity unpinned".
 """
 from .masks import MaskLayout, RectMask, allowed, chunk_over_cache, key_ranges, dense_mask, unmasked_pairs
-from .attention_jvp import attn_jvp_ref, unmasked_pairs_rows
+from .attention_jvp import attn_jvp_ref
 from .attention_vjp import attn_vjp_ref, attn_vjp_sampled
 
 __all__ = [
     "MaskLayout", "RectMask", "allowed", "chunk_over_cache", "key_ranges", "dense_mask", "unmasked_pairs",
-    "attn_jvp_ref", "unmasked_pairs_rows", "attn_vjp_ref", "attn_vjp_sampled",
+    "attn_jvp_ref", "attn_vjp_ref", "attn_vjp_sampled",
 ]

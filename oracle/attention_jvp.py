@@ -98,7 +98,3 @@ def attn_jvp_ref(q, k, v, tq, tk, tv, mask, scale: Optional[float] = None,
             o[:, :, n], to[:, :, n], lse[:, :, n] = o[:, :, ns[0]], to[:, :, ns[0]], lse[:, :, ns[0]]
     return o, to, lse
 
-
-def unmasked_pairs_rows(mask, rows: Iterable[int]) -> int:
-    """Allowed (query, key) pairs over the given rows, for FLOP accounting."""
-    return sum(b - a for i in rows for (a, b) in key_ranges(mask, int(i)))

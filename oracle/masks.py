@@ -5,8 +5,9 @@ descriptor builder: this file states *which* (query, key) pairs are allowed,
 token by token, and nothing about tiles.
 
 Source: "Causal-rCM" Sec. 2.3 (causal attention across frames / chunks),
-Sec. 3.1.1 and Eq. 8 (teacher forcing packs [clean | noisy]; a noisy block sees
-its allowed clean history and its own noisy tokens), App. B (a mask is a set of
+Sec. 3.1.1 and Eq. 8 (teacher forcing packs [clean | noisy]; each noisy block
+attends to the clean frames before it that it may use, plus the tokens of its
+own noisy block), App. B (a mask is a set of
 admissible query-key rectangles), and the reading notes' mask table (full
 within a frame, causal across frames; block-causal is full within a chunk and
 causal across chunks).
