@@ -10,6 +10,11 @@ missing, every call raises.
     desc = attn_jvp_mask_desc_build("block_causal", num_frames=21, frame_tokens=1560,
                                     frames_per_chunk=3, head_dim=128, dtype="bf16")
     o, to, lse = attn_jvp_fwd(q, k, v, tq, tk, tv, desc)
+
+The builders copy the descriptor's tables to the current GPU (``device="auto"``)
+so that the launches themselves never allocate; pass ``device=None`` to build
+on the host only and call ``desc.upload(device)`` later.  A descriptor must
+outlive every HIP graph that captured a launch using it.
 """
 from __future__ import annotations
 
@@ -21,7 +26,7 @@ from typing import Optional, Sequence, Tuple
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattnjvp.so")
 
-AJ_OK, AJ_EINVAL, AJ_ENOTSUP, AJ_ENOMEM, AJ_EHIP, AJ_EMASK = range(6)
+AJ_OK, AJ_EINVAL, AJ_ENOTSUP, AJ_ENOMEM, AJ_EHIP, AJ_EMASK, AJ_ENOTLOADED = range(7)
 AJ_F32, AJ_BF16 = 0, 1
 MASK_KINDS = {"full": 0, "block_causal": 1, "frame_causal": 1, "tf_clean_noisy": 2}
 DTYPES = {"f32": AJ_F32, "float32": AJ_F32, "bf16": AJ_BF16, "bfloat16": AJ_BF16}
@@ -92,11 +97,12 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_kv.argtypes = [ctypes.POINTER(aj_kv_shape), P, P, P, pdesc, f32, P, P, P]
     L.attn_jvp_mask_desc_from_rects_kv.argtypes = [i32, i32, P, i32, i32, i32, ctypes.POINTER(pdesc)]
     L.attn_jvp_mask_desc_col_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
+    L.attn_jvp_mask_desc_upload.argtypes = [pdesc, i32]
     for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
                "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
                "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
                "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits", "attn_fwd_kv",
-               "attn_jvp_mask_desc_from_rects_kv"):
+               "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_mask_desc_upload"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -179,6 +185,21 @@ class MaskDesc:
                "attn_jvp_mask_desc_col_bits")
         return b.value
 
+    def upload(self, device=None) -> "MaskDesc":
+        """Copies the tables to a GPU (default: torch's current device); once per
+        device, before the first launch there and outside any graph capture."""
+        import torch
+
+        if device is None:
+            index = torch.cuda.current_device()
+        else:
+            dv = torch.device(device) if not isinstance(device, int) else torch.device("cuda", device)
+            if dv.type != "cuda":
+                raise ValueError(f"descriptor tables go to a GPU, not {dv}")
+            index = torch.cuda.current_device() if dv.index is None else dv.index
+        _check(lib().attn_jvp_mask_desc_upload(self.handle, int(index)), "attn_jvp_mask_desc_upload")
+        return self
+
     def close(self) -> None:
         if self._h:
             attn_jvp_mask_desc_free(self._h)
@@ -189,6 +210,20 @@ class MaskDesc:
             self.close()
         except Exception:
             pass
+
+
+def _place(desc: MaskDesc, device) -> MaskDesc:
+    """Uploads a new descriptor: device "auto" = torch's current GPU if there is
+    one (none: host-only), None = host-only, else that device."""
+    if device is None:
+        return desc
+    if isinstance(device, str) and device == "auto":
+        import torch
+
+        if not torch.cuda.is_available():
+            return desc
+        device = None
+    return desc.upload(device)
 
 
 def _flatten(items, width: int, what: str):
@@ -203,8 +238,10 @@ def _flatten(items, width: int, what: str):
 
 
 def attn_jvp_mask_desc_build(kind: str, num_frames: int, frame_tokens: int, frames_per_chunk: int = 1,
-                             head_dim: int = 128, dtype="bf16", seq_len: Optional[int] = None) -> MaskDesc:
-    """Descriptor for a frame-level layout (see ``aj_mask_kind`` in the header)."""
+                             head_dim: int = 128, dtype="bf16", seq_len: Optional[int] = None,
+                             device="auto") -> MaskDesc:
+    """Descriptor for a frame-level layout (see ``aj_mask_kind`` in the header),
+    uploaded to ``device`` (see ``_place``)."""
     k = MASK_KINDS[kind] if isinstance(kind, str) else int(kind)
     spec = aj_mask_spec(k, num_frames, frame_tokens, frames_per_chunk)
     if seq_len is None:
@@ -213,11 +250,11 @@ def attn_jvp_mask_desc_build(kind: str, num_frames: int, frame_tokens: int, fram
     dt = _dtype_code(dtype)
     _check(lib().attn_jvp_mask_desc_build(ctypes.byref(spec), seq_len, head_dim, dt, ctypes.byref(out)),
            "attn_jvp_mask_desc_build")
-    return MaskDesc(out.value, head_dim, dt)
+    return _place(MaskDesc(out.value, head_dim, dt), device)
 
 
 def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], head_dim: int = 128,
-                                  dtype="bf16") -> MaskDesc:
+                                  dtype="bf16", device="auto") -> MaskDesc:
     """Descriptor from disjoint half-open rectangles (q0, q1, k0, k1)."""
     flat = _flatten(rects, 4, "rectangle")
     arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
@@ -226,11 +263,11 @@ def attn_jvp_mask_desc_from_rects(seq_len: int, rects: Sequence[Sequence[int]], 
     _check(lib().attn_jvp_mask_desc_from_rects(seq_len, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 4,
                                                head_dim, dt, ctypes.byref(out)),
            "attn_jvp_mask_desc_from_rects")
-    return MaskDesc(out.value, head_dim, dt)
+    return _place(MaskDesc(out.value, head_dim, dt), device)
 
 
 def attn_jvp_mask_desc_from_rects_kv(q_len: int, kv_len: int, rects: Sequence[Sequence[int]], head_dim: int = 128,
-                                     dtype="bf16") -> MaskDesc:
+                                     dtype="bf16", device="auto") -> MaskDesc:
     """Descriptor for a query chunk of q_len tokens over kv_len cached keys, from
     disjoint half-open rectangles (q0, q1, k0, k1)."""
     flat = _flatten(rects, 4, "rectangle")
@@ -240,10 +277,10 @@ def attn_jvp_mask_desc_from_rects_kv(q_len: int, kv_len: int, rects: Sequence[Se
     _check(lib().attn_jvp_mask_desc_from_rects_kv(q_len, kv_len, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 4,
                                                   head_dim, dt, ctypes.byref(out)),
            "attn_jvp_mask_desc_from_rects_kv")
-    return MaskDesc(out.value, head_dim, dt)
+    return _place(MaskDesc(out.value, head_dim, dt), device)
 
 
-def attn_jvp_mask_desc_tangent_free(base: MaskDesc, ranges: Sequence[Sequence[int]]) -> MaskDesc:
+def attn_jvp_mask_desc_tangent_free(base: MaskDesc, ranges: Sequence[Sequence[int]], device="auto") -> MaskDesc:
     """Descriptor with base's mask that declares tq, tk, tv zero on the token
     ranges [t0, t1) (see the header); the JVP then skips the zero products."""
     flat = _flatten(ranges, 2, "range")
@@ -252,7 +289,7 @@ def attn_jvp_mask_desc_tangent_free(base: MaskDesc, ranges: Sequence[Sequence[in
     _check(lib().attn_jvp_mask_desc_tangent_free(base.handle, ctypes.cast(arr, ctypes.c_void_p), len(flat) // 2,
                                                  ctypes.byref(out)),
            "attn_jvp_mask_desc_tangent_free")
-    return MaskDesc(out.value, base.head_dim, base.dtype)
+    return _place(MaskDesc(out.value, base.head_dim, base.dtype), device)
 
 
 def attn_jvp_mask_desc_free(handle) -> None:
@@ -424,7 +461,7 @@ def attn_bwd(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = Non
 
 
 __all__ = [
-    "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_F32", "AJ_BF16",
+    "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_ENOTLOADED", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
     "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
     "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_fwd", "attn_fwd_kv", "attn_bwd", "LIB_PATH",

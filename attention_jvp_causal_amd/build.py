@@ -37,14 +37,16 @@ SOURCE_FLAGS = {
 
 def compile_flags(src: str | None = None):
     """hipcc flags shared by every source, plus the per-source ones for `src`."""
+    hip = src is None or src.endswith(".hip")
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: plain float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         # kernels never produce NaN (masked scores are -inf and guarded), so
-        # fmaxf needs no NaN canonicalisation
-        "-fno-honor-nans",
+        # fmaxf needs no NaN canonicalisation; the host sources keep IEEE NaN
+        # semantics (their argument checks test for NaN)
+        *(["-fno-honor-nans"] if hip else []),
         # MFMA accumulators in VGPRs: the online-softmax rescale multiplies them
         # with VALU ops, which cannot address AGPRs
         "-mllvm", "-amdgpu-mfma-vgpr-form=1",

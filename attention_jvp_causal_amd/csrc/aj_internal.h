@@ -1,47 +1,23 @@
-// Internal definitions shared by the host side of the attention-JVP library:
-// the mask descriptor (tile map built from admissible rectangles) and the
-// kernel launch arguments.  Not part of the public C ABI.
+// Host-side internals of the attention-JVP library: the mask descriptor (tile
+// maps built from admissible rectangles) and its device tables.  Not part of
+// the public C ABI.
 #pragma once
 
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
 #include "../../include/attn_jvp.h"
+#include "aj_tiles.h"
 
 namespace aj {
 
-// Tile geometry of the kernels.  Every instantiation (bf16 / fp32, D = 64 / 128)
-// uses 128 query rows per workgroup and 64 keys per streamed tile, so one key
-// bitmask row is one 64-bit word.
-constexpr int kTileM = 128;
-constexpr int kTileN = 64;
 constexpr int kMaxDevices = 64;
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_dtype(int t) { return t == AJ_F32 || t == AJ_BF16; }
-
-// Which tangents a (query tile, key tile) pair carries, from the caller's
-// declaration of tokens whose tangents are zero (Entry::flags):
-//   kTileJvp       the general case: every product of the JVP
-//   kTileKeysFree  tK = tV = 0 on every key of the tile: tS = c tQ K^T and
-//                  (A + B) gets only (P.tS) V
-//   kTileAllFree   tQ = tK = tV = 0 for the whole tile: tS = 0, so only the
-//                  primal products remain
-// A query-tangent-free tile whose keys carry tangents runs as kTileJvp (tQ is
-// zero there and simply multiplies in).
-constexpr int32_t kTileJvp = 0;
-constexpr int32_t kTileKeysFree = 1;
-constexpr int32_t kTileAllFree = 3;
-
-// One run of key tiles visited by a query tile.  pidx < 0: every tile in
-// [kt0, kt1) is full.  pidx >= 0: the single tile kt0 (kt1 = kt0 + 1) is
-// partial and its per-row key bitmask starts at bits[pidx * kTileM].  Every
-// tile of a run has the same flags (one of the kTile* variants).
-struct Entry {
-  int32_t kt0, kt1, pidx, flags;
-};
 
 // A tile map over one orientation of the mask: for every tile of kTileM
 // rows (the "owner" axis) the runs of kTileN-wide tiles of the other axis it
@@ -64,17 +40,12 @@ struct TileMap {
   std::vector<uint64_t> bits;       // partial_tiles * kTileM words
 };
 
-struct DeviceMap {
-  const int32_t* qt_off = nullptr;
-  const Entry* entries = nullptr;
-  const int32_t* tasks = nullptr;
-  const int32_t* tasks_split = nullptr;
-  const uint64_t* bits = nullptr;
-};
-
 struct DeviceTables {
   void* base = nullptr;  // one hipMalloc holding both maps
   DeviceMap rows, cols;
+  // set once base and the maps are valid (attn_jvp_mask_desc_upload); launches
+  // read the tables without taking the descriptor's lock
+  std::atomic<bool> ready{false};
 };
 
 }  // namespace aj
@@ -88,7 +59,7 @@ struct aj_mask_desc {
   std::vector<int32_t> tfree;       // merged tangent-free token ranges {t0,t1}
   aj::TileMap rows;                 // query tiles -> key-tile runs
   aj::TileMap cols;                 // key tiles -> query-tile runs (transposed mask)
-  std::mutex mu;                    // guards dev[]
+  std::mutex mu;                    // serialises uploads into dev[]
   aj::DeviceTables dev[aj::kMaxDevices];
 };
 

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "aj_internal.h"
+#include "aj_tiles.h"
 
 namespace aj {
 

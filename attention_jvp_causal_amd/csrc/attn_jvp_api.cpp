@@ -20,19 +20,35 @@ constexpr int32_t kVersion = 1 * 10000 + 0 * 100 + 0;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Uploads the descriptor's tables to the current device once; returns the
-// device copy or an error status.
-int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
-  aj_mask_desc* d = const_cast<aj_mask_desc*>(cd);
+// A usable softmax scale: finite and > 0.  Tested on the bit pattern (sign
+// clear, exponent not all ones, not zero), so the check holds under any
+// floating-point model the compiler is given.
+bool valid_scale(float scale) {
+  uint32_t u = 0;
+  std::memcpy(&u, &scale, sizeof u);
+  return (u >> 31) == 0 && (u & 0x7f800000u) != 0x7f800000u && (u & 0x7fffffffu) != 0;
+}
+
+// The descriptor's tables on the current device, as attn_jvp_mask_desc_upload
+// left them.  A lookup only: allocates, copies and synchronises nothing, so a
+// launch that calls it may be captured into a HIP graph.
+int32_t device_tables(const aj_mask_desc* d, const DeviceTables** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return AJ_EHIP;
   if (dev < 0 || dev >= aj::kMaxDevices) return AJ_ENOTSUP;
+  const DeviceTables& t = d->dev[dev];
+  if (!t.ready.load(std::memory_order_acquire)) return AJ_ENOTLOADED;
+  *out = &t;
+  return AJ_OK;
+}
+
+// Copies the descriptor's tables to device `dev` (one hipMalloc, one blocking
+// hipMemcpy), unless they are there already.  The caller has made `dev`
+// current.
+int32_t upload_tables(aj_mask_desc* d, int dev) {
   std::lock_guard<std::mutex> lock(d->mu);
   DeviceTables& t = d->dev[dev];
-  if (t.base) {
-    *out = &t;
-    return AJ_OK;
-  }
+  if (t.ready.load(std::memory_order_acquire)) return AJ_OK;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   // layout: [rows map | cols map], each {qt_off | entries | tasks | tasks_split | bits}
   struct Part {
@@ -71,7 +87,7 @@ int32_t device_tables(const aj_mask_desc* cd, const DeviceTables** out) {
     dm[i]->bits = reinterpret_cast<const uint64_t*>(b + parts[5 * i + 4].off);
   }
   t.base = base;
-  *out = &t;
+  t.ready.store(true, std::memory_order_release);
   return AJ_OK;
 }
 
@@ -102,7 +118,7 @@ int32_t prepare_geom(const Geometry& s, const void* const* ins, int n_in, const 
   for (int i = 0; i < n_out; ++i)
     if (!outs[i] || !aligned16(outs[i])) return AJ_EINVAL;
   if (s.B < 1 || s.H < 1 || s.Lq < 1 || s.Lk < 1) return AJ_EINVAL;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return AJ_EINVAL;
+  if (!valid_scale(scale)) return AJ_EINVAL;
   if (!aj::supported_head_dim(s.D)) return AJ_ENOTSUP;
   if (!aj::supported_dtype(s.in_dtype) || !aj::supported_dtype(s.out_dtype)) return AJ_ENOTSUP;
   if (s.in_dtype == AJ_F32 && s.out_dtype != AJ_F32) return AJ_ENOTSUP;
@@ -175,6 +191,7 @@ const char* attn_jvp_status_str(int32_t status) {
     case AJ_ENOMEM: return "AJ_ENOMEM: allocation failed";
     case AJ_EHIP: return "AJ_EHIP: HIP runtime error";
     case AJ_EMASK: return "AJ_EMASK: invalid mask or descriptor mismatch";
+    case AJ_ENOTLOADED: return "AJ_ENOTLOADED: descriptor not uploaded to the current device";
     default: return "unknown status";
   }
 }
@@ -223,6 +240,25 @@ int32_t attn_jvp_mask_desc_tangent_free(const aj_mask_desc* base, const int32_t*
   } catch (...) {
     return AJ_EINVAL;
   }
+}
+
+int32_t attn_jvp_mask_desc_upload(aj_mask_desc* d, int32_t device) {
+  if (!d) return AJ_EINVAL;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) return AJ_EHIP;
+  if (device < 0 || device >= n) return AJ_EINVAL;
+  if (device >= aj::kMaxDevices) return AJ_ENOTSUP;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return AJ_EHIP;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return AJ_EHIP;
+  int32_t st = AJ_OK;
+  try {
+    st = upload_tables(d, device);
+  } catch (const std::bad_alloc&) {
+    st = AJ_ENOMEM;
+  }
+  if (cur != device) (void)hipSetDevice(cur);
+  return st;
 }
 
 int32_t attn_jvp_mask_desc_work(const aj_mask_desc* d, int64_t* pairs_by_variant) {
@@ -294,7 +330,7 @@ void attn_jvp_mask_desc_free(aj_mask_desc* d) {
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (int dev = 0; dev < aj::kMaxDevices; ++dev) {
-    if (!d->dev[dev].base) continue;
+    if (!d->dev[dev].ready.load(std::memory_order_acquire)) continue;
     if (hipSetDevice(dev) == hipSuccess) (void)hipFree(d->dev[dev].base);
   }
   if (have_cur) (void)hipSetDevice(cur);

@@ -34,7 +34,6 @@
 #include <type_traits>
 
 #include "aj_device.h"
-#include "aj_internal.h"
 #include "aj_launch.h"
 
 namespace aj {

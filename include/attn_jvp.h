@@ -27,7 +27,11 @@
  *  - No C++ exception crosses this boundary.
  *  - Device pointers are owned by the caller; the library never frees or
  *    retains them.  Mask descriptors are owned by the library (create with a
- *    builder, release with attn_jvp_mask_desc_free).
+ *    builder, copy to a device with attn_jvp_mask_desc_upload, release with
+ *    attn_jvp_mask_desc_free).
+ *  - The launch entry points allocate no memory, copy nothing and do not
+ *    synchronise: they validate, look up the descriptor's device tables and
+ *    enqueue kernels.
  */
 #ifndef ATTN_JVP_H_
 #define ATTN_JVP_H_
@@ -44,7 +48,9 @@ typedef enum {
   AJ_ENOTSUP = 2,  /* valid but unsupported: head_dim not in {64, 128}, dtype pair not built */
   AJ_ENOMEM = 3,   /* host or device allocation failed */
   AJ_EHIP = 4,     /* a HIP runtime call failed (no device, launch failure, ...) */
-  AJ_EMASK = 5     /* mask specification invalid, or descriptor does not match the call */
+  AJ_EMASK = 5,    /* mask specification invalid, or descriptor does not match the call */
+  AJ_ENOTLOADED = 6 /* the descriptor's tables are not on the current device:
+                       call attn_jvp_mask_desc_upload first */
 } aj_status;
 
 /* Element types of Q, K, V, tQ, tK, tV (in) and O, tO (out). */
@@ -76,9 +82,10 @@ typedef struct {
 
 /* Opaque descriptor: the mask as a tile-level skip / partial / full map over
  * the kernel's query and key tiles, per-row key bitmasks for partial tiles and
- * a longest-first task order.  Immutable after creation; may be shared by
- * threads and streams.  Device copies of its tables are made on first use on
- * each device and freed by attn_jvp_mask_desc_free. */
+ * a longest-first task order.  Its mask and tables are immutable after
+ * creation; it may be shared by threads and streams.  Device copies of the
+ * tables are made by attn_jvp_mask_desc_upload, once per device, and freed by
+ * attn_jvp_mask_desc_free. */
 typedef struct aj_mask_desc aj_mask_desc;
 
 typedef struct {
@@ -128,6 +135,20 @@ int32_t attn_jvp_mask_desc_from_rects(int32_t seq_len, const int32_t* rects, int
 int32_t attn_jvp_mask_desc_from_rects_kv(int32_t q_len, int32_t kv_len, const int32_t* rects, int32_t n_rects,
                                          int32_t head_dim, int32_t dtype, aj_mask_desc** out);
 
+/* Copy a descriptor's tables to GPU `device` (App. B, "Sparse custom-mask
+ * representation": the mask reaches the kernel as a precomputed list of
+ * admissible ranges; this call puts that list in device memory).  The launch
+ * entry points (attn_jvp_fwd, attn_fwd, attn_fwd_kv, attn_bwd) read the tables
+ * of the device current at the call and never allocate or copy them: call
+ * this once per device before the first launch, outside any HIP-graph
+ * capture.  Allocates device memory (hipMalloc) and copies synchronously
+ * (hipMemcpy); restores the caller's current device.  A second call for the
+ * same device does nothing and returns AJ_OK; calls from several threads are
+ * serialised.  Errors: AJ_EINVAL (null desc, device out of range), AJ_ENOTSUP
+ * (device index >= 64), AJ_ENOMEM (device or host allocation failed), AJ_EHIP
+ * (no device, copy failed). */
+int32_t attn_jvp_mask_desc_upload(aj_mask_desc* desc, int32_t device);
+
 /* Derive a descriptor that also knows which tokens carry no tangent.
  * In teacher-forcing sCM / MeanFlow the JVP runs through the packed
  * [clean | noisy] forward and the clean context has zero tangent (Sec. 3.1.2);
@@ -145,8 +166,8 @@ int32_t attn_jvp_mask_desc_from_rects_kv(int32_t q_len, int32_t kv_len, const in
  * lie inside the ranges) run the primal forward of attn_fwd, which writes
  * tO = 0 for them, in a launch of their own before the JVP kernel's.  The
  * result equals attn_jvp_fwd with the plain descriptor whenever the
- * declaration holds: bit for bit, except that at head_dim 128 O and lse of
- * the primal-only query tiles agree to rounding (as attn_fwd's do); if the
+ * declaration holds: bit for bit, except that O and lse of the primal-only
+ * query tiles agree to rounding (as attn_fwd's do); if the
  * declaration does not hold, the tangent output is unspecified.  Host-only.
  * Errors: AJ_EINVAL (null pointers, bad range), AJ_ENOMEM.  On error *out is
  * set to NULL. */
@@ -189,9 +210,10 @@ int32_t attn_jvp_mask_desc_row_bits(const aj_mask_desc* desc, int32_t q_tile, in
 int32_t attn_jvp_mask_desc_col_bits(const aj_mask_desc* desc, int32_t k_tile, int32_t q_tile, int32_t key_row,
                                     uint64_t* bits);
 
-/* Release a descriptor and its device tables on every device that used it.
- * Must not be called while a launch that uses it may still run.  NULL is a
- * no-op. */
+/* Release a descriptor and its device tables on every device it was uploaded
+ * to.  Must not be called while a launch that uses it may still run, nor while
+ * a HIP graph that captured such a launch may still be replayed (the graph
+ * holds the addresses of the tables).  NULL is a no-op. */
 void attn_jvp_mask_desc_free(aj_mask_desc* desc);
 
 /* Shapes and strides of one call.  Strides are in elements.  The six inputs
@@ -215,14 +237,19 @@ typedef struct {
  * size < 2^31.  scale multiplies the scores and their tangents;
  * pass 1/sqrt(D) for the usual softmax scale.  Rows with no allowed key get
  * O = tO = 0 and lse = -inf.  Input values at masked-out positions must be
- * finite (they are read for partial tiles and multiplied by zero).
+ * finite (they are read for partial tiles and multiplied by zero).  At
+ * head_dim 64 with bf16 inputs the value products run in fp16: V and tV
+ * must lie within fp16's range (|x| <= 65504; larger magnitudes saturate)
+ * and |scale * (<tq, k> + <q, tk>)| must stay below 65504.
  * The outputs must not overlap the inputs.
  * Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and runs
  * asynchronously; device faults surface at the caller's next synchronisation.
- * The first call on a device with a given descriptor uploads its tables
- * (synchronous hipMalloc/hipMemcpy, once).
+ * The descriptor must have been uploaded to the current device
+ * (attn_jvp_mask_desc_upload).  The call only enqueues kernels: it allocates,
+ * copies and synchronises nothing, so it may be captured into a HIP graph.
  * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK (desc seq_len / head_dim / dtype
- * differ from the call), AJ_EHIP, AJ_ENOMEM. */
+ * differ from the call), AJ_ENOTLOADED (desc not uploaded to the current
+ * device), AJ_EHIP. */
 int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const void* v,
                      const void* tq, const void* tk, const void* tv, const aj_mask_desc* mask,
                      float scale, void* o, void* to, float* lse, void* stream);
@@ -230,11 +257,11 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
 /* Primal masked attention (Eq. 42): O = softmax(scale * Q K^T + M) V and lse,
  * the forward of the student's packed teacher-forcing attention (Sec. 3.1.1,
  * Eq. 8) on the same descriptor as the JVP.  Same shapes, strides and checks
- * as attn_jvp_fwd; O and lse equal attn_jvp_fwd's bit for bit at head_dim 64
- * (the same kernel code without the tangent products) and to rounding at 128
- * (32-row waves instead of the JVP's 16).  in_dtype must be AJ_BF16
+ * as attn_jvp_fwd; O and lse agree with attn_jvp_fwd's to rounding (at
+ * head_dim 128 32-row waves instead of the JVP's 16; at 64 the JVP runs its
+ * value products in fp16, this kernel in bf16).  in_dtype must be AJ_BF16
  * (AJ_ENOTSUP otherwise).  o is [B, H, L, D] out_dtype, lse [B, H, L] float32.
- * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
+ * Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_ENOTLOADED, AJ_EHIP. */
 int32_t attn_fwd(const aj_shape* shape, const void* q, const void* k, const void* v, const aj_mask_desc* mask,
                  float scale, void* o, float* lse, void* stream);
 
@@ -253,7 +280,7 @@ typedef struct {
 /* Primal masked attention of a query chunk over a KV cache (readonly mode of
  * Sec. 3.2.1: the chunk being generated attends the committed prefix, and
  * itself once its keys sit in the cache slots after the prefix).  Same
- * operation, kernels, checks and errors as attn_fwd with the key length and
+ * operation, kernels, checks, errors and upload requirement as attn_fwd with the key length and
  * strides taken from the shape; the descriptor must have been built for
  * (q_len, kv_len).  lse is [B, H, q_len] float32.  in_dtype must be AJ_BF16. */
 int32_t attn_fwd_kv(const aj_kv_shape* shape, const void* q, const void* k, const void* v,
@@ -274,7 +301,8 @@ int32_t attn_fwd_kv(const aj_kv_shape* shape, const void* q, const void* k, cons
  * kernels read it back).  Two kernels run in order on `stream`; no atomics,
  * the result is deterministic.  Same checks as attn_jvp_fwd; in_dtype must be
  * AJ_BF16 (AJ_ENOTSUP otherwise).  Outputs must not overlap the inputs or
- * each other.  Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_EHIP, AJ_ENOMEM. */
+ * each other.  Errors: AJ_EINVAL, AJ_ENOTSUP, AJ_EMASK, AJ_ENOTLOADED,
+ * AJ_EHIP. */
 int32_t attn_bwd(const aj_shape* shape, const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
                  void* dk, void* dv, float* delta, void* stream);

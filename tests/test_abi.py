@@ -18,7 +18,7 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails v
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_jvp_\w+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(6):
+    for code in range(7):
         s = aj.status_str(code)
         assert s.startswith("AJ_")
     assert aj.status_str(99) == "unknown status"
@@ -153,6 +153,9 @@ def test_fwd_rejects_bad_arguments_before_launch():
     assert _fwd(_shape(), h, scale=float("inf")) == E.AJ_EINVAL
     assert _fwd(_shape(), h, scale=0.0) == E.AJ_EINVAL
     assert _fwd(_shape(), h, scale=-0.1) == E.AJ_EINVAL
+    assert _fwd(_shape(), h, scale=-0.0) == E.AJ_EINVAL
+    assert _fwd(_shape(), h, scale=float("-inf")) == E.AJ_EINVAL
+    assert _fwd(_shape(), h, scale=-float("nan")) == E.AJ_EINVAL
     assert _fwd(_shape(D=96), h) == E.AJ_ENOTSUP
     assert _fwd(_shape(idt=aj.AJ_F32, odt=aj.AJ_BF16), df32.handle) == E.AJ_ENOTSUP
     assert _fwd(_shape(idt=3), h) == E.AJ_ENOTSUP
@@ -260,3 +263,20 @@ def test_kv_entry_point_without_gpu_reports_hip_error():
         pytest.skip("a GPU is present; a valid call would launch")
     kv = aj.attn_jvp_mask_desc_from_rects_kv(64, 100, [(0, 64, 0, 100)], head_dim=128, dtype="bf16")
     assert _fwd_kv(_kvshape(), kv.handle) == aj.AJ_EHIP
+
+
+def test_upload_rejects_bad_arguments():
+    assert aj.lib().attn_jvp_mask_desc_upload(None, 0) == aj.AJ_EINVAL
+    d = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16", device=None)
+    assert aj.lib().attn_jvp_mask_desc_upload(d.handle, -1) in (aj.AJ_EINVAL, aj.AJ_EHIP)
+    import torch
+    if torch.cuda.is_available():
+        n = torch.cuda.device_count()
+        assert aj.lib().attn_jvp_mask_desc_upload(d.handle, n) == aj.AJ_EINVAL
+    else:
+        # no GPU: the device count is unavailable
+        assert aj.lib().attn_jvp_mask_desc_upload(d.handle, 0) == aj.AJ_EHIP
+        # and the auto placement of the builders leaves the descriptor host-only
+        d2 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16")
+        assert d2.stats()["seq_len"] == 64
+

@@ -1,9 +1,9 @@
 """The launch paths under HIP graph capture.
 
-After a first call (which uploads the descriptor's tables), attn_jvp_fwd (also
-with a tangent-free descriptor: two launches), attn_fwd, attn_fwd_kv and
+The descriptor builders upload the tables to the GPU; after that attn_jvp_fwd
+(also with a tangent-free descriptor: two launches), attn_fwd, attn_fwd_kv and
 attn_bwd enqueue kernels only: no allocation, no memset, no host
-synchronisation.  They are captured into a graph on torch's capture stream and
+synchronisation, from the very first call on.  They are captured into a graph on torch's capture stream and
 the graph is replayed several times, with eager work and synchronisation in
 between; every replay must reproduce the eager results bit for bit (the
 kernels are deterministic).
@@ -41,7 +41,7 @@ def test_jvp_and_gradients_replay_from_a_graph():
         aj.attn_bwd(dev["q"], dev["k"], dev["v"], fwd_out[0], d_out, fwd_out[1], desc, scale=w.scale,
                     out_dtype=torch.float32, out=bwd_out)
 
-    run()  # eager; uploads the tables
+    run()  # eager reference
     torch.cuda.synchronize()
     want = [t.clone() for t in jvp_out + fwd_out + bwd_out]
 
@@ -89,7 +89,7 @@ def test_tangent_free_path_and_kv_forward_replay_from_a_graph():
         aj.attn_jvp_fwd(*(dev[n] for n in NAMES), fast, scale=w.scale, out=jvp_out)
         aj.attn_fwd_kv(q_chunk, dev["k"], dev["v"], kv_desc, scale=w.scale, out=kv_out)
 
-    run()  # eager; uploads the tables
+    run()  # eager reference
     torch.cuda.synchronize()
     want = [t.clone() for t in jvp_out + kv_out]
     assert bool((want[1][:, :, : L // 2] == 0).all())  # tO on the declared tangent-free rows
@@ -112,3 +112,57 @@ def test_tangent_free_path_and_kv_forward_replay_from_a_graph():
         torch.cuda.synchronize()
         for got, ref in zip(jvp_out + kv_out, want):
             assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
+
+
+def test_first_launch_of_a_fresh_descriptor_is_captured():
+    # Fresh descriptors whose first launch ever happens inside the capture:
+    # the builders uploaded their tables, so the launches only enqueue kernels.
+    # A descriptor built host-only is refused inside the capture with a status
+    # code, enqueues nothing, and the capture goes on.
+    w = Workload("graph_first", 1, 3, 64, "bf16", "block_causal", 6, 70, 2, seed=162)
+    dev = {n: t.cuda() for n, t in make_inputs(w).items()}
+    B, H, L, D = w.shape
+    mk = lambda device: aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                                    head_dim=D, dtype=w.dtype, device=device)
+    desc, desc_f = mk("auto"), mk("auto")
+    host_only = mk(None)
+    jvp_out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    fwd_out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    refused = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    print("[case] first launch of fresh descriptors under capture", flush=True)
+    with torch.cuda.stream(s):
+        for t in jvp_out + fwd_out + refused:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, scale=w.scale, out=jvp_out)
+            with pytest.raises(aj.AttnJvpError) as e:
+                aj.attn_fwd(dev["q"], dev["k"], dev["v"], host_only, scale=w.scale, out=refused)
+            assert e.value.status == aj.AJ_ENOTLOADED
+            aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc_f, scale=w.scale, out=fwd_out)
+    torch.cuda.synchronize()
+    # eager references, after the capture
+    want_jvp = aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, scale=w.scale)
+    want_fwd = aj.attn_fwd(dev["q"], dev["k"], dev["v"], desc_f, scale=w.scale)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in jvp_out + fwd_out:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(jvp_out + fwd_out, want_jvp + want_fwd):
+            assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
+        assert all(bool(t.isnan().all()) for t in refused), "the refused call must write nothing"
+    # once uploaded, the host-only descriptor gives the same result
+    host_only.upload()
+    o, lse = aj.attn_fwd(dev["q"], dev["k"], dev["v"], host_only, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, want_fwd[0]) and torch.equal(lse, want_fwd[1])
