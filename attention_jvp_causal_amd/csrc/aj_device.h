@@ -7,13 +7,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "aj_internal.h"
+#include "aj_tiles.h"
 
 namespace aj {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -187,6 +189,31 @@ __device__ __forceinline__ float row4_sum(float x) {
 // Lazy rescale of the online softmax: a row's reference max moves only when
 // its max grows by more than 2^8 (log2 units).
 constexpr float kLazyRescaleLog2 = 8.0f;
+
+// Rewrites, in place, the 16-byte chunks of two key tiles (V and tV) that this
+// wave's lanes brought in by DMA (issue_tile_loads: wave instruction i of lane
+// l fills chunk (wave + NW i) * 64 + l of each tensor tile) from bf16 to fp16.
+// Every bf16 value of magnitude in [2^-14, 65504] is an fp16 value, so the
+// conversion is exact there; smaller magnitudes keep fp16's subnormal
+// resolution (2^-24) and larger ones saturate to 65504 (round toward zero).
+// Called after the wave's own DMA has landed (vmcnt 0) and before the barrier
+// that publishes the buffer, so no other wave reads these chunks meanwhile.
+template <int NW, int D>
+__device__ __forceinline__ void bf16_chunks_to_f16(uint16_t* t0, uint16_t* t1, int wave, int lane) {
+  constexpr int NI = TileLoadPlan<NW, D>::NI;
+#pragma unroll
+  for (int i = 0; i < 2 * NI; ++i) {
+    uint16_t* p = (i < NI ? t0 : t1) + (wave + NW * (i % NI)) * 512 + 8 * lane;
+    const u32x4_t x = *(const u32x4_t*)p;
+    u32x4_t y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = __uint_as_float(x[w] << 16), hi = __uint_as_float(x[w] & 0xffff0000u);
+      y[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    *(u32x4_t*)p = y;
+  }
+}
 
 // Key-tile buffers of the bf16 kernels: NT = 4 tensors (K, tK, V, tV) for the
 // JVP, NT = 2 (K, V) for the primal forward, whose smaller footprint lets two

@@ -33,8 +33,8 @@
 
 #include <type_traits>
 
+#include "../../include/attn_jvp.h"
 #include "aj_device.h"
-#include "aj_internal.h"
 #include "aj_launch.h"
 
 namespace aj {

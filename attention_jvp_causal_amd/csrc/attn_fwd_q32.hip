@@ -12,8 +12,8 @@
 #include <cmath>
 #include <type_traits>
 
+#include "../../include/attn_jvp.h"
 #include "aj_device.h"
-#include "aj_internal.h"
 #include "aj_launch.h"
 
 namespace aj {
@@ -35,6 +35,14 @@ constexpr int NTHREADS = 64 * NWAVES;
 // are stored at chunk position c ^ swz_q32(r) (aj_device.h).
 
 constexpr int kWavesQ32 = 4;
+
+// v_mfma_f32_32x32x16 with bf16 or fp16 operands
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // ---- q32 shape --------------------------------------------------------------
 
@@ -58,6 +66,17 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
   constexpr int NT = JVP ? 4 : 2;
   using Lds = Bf16Lds<D, NT>;
+  // The JVP runs its value products in fp16: V and tV are converted in LDS
+  // (exact for bf16 values of magnitude in [2^-14, 65504]), and p~ 2^-8 and
+  // u = p~ 2^-8 (c ts) are rounded to fp16 (11 significant bits against
+  // bf16's 8).  The tangent's A - mu O cancellation is sensitive to the
+  // rounding of both p~ (through O) and u; in fp16 their error is eight times
+  // smaller.  The 2^-8 keeps p~ 2^-8 <= 1 under the lazy rescale (p~ <= 2^8),
+  // so u stays finite for |c ts| < 65504.  The primal kernel stays in bf16.
+  constexpr bool F16 = JVP;
+  typedef std::conditional_t<F16, f16x8_t, bf16x8_t> op8_t;
+  typedef std::conditional_t<F16, f16x2_t, bf16x2_t> op2_t;
+  constexpr float kPScaleLog2 = F16 ? 8.0f : 0.0f;  // p~ is stored as p~ 2^-kPScaleLog2
   __shared__ __attribute__((aligned(1024))) Lds s;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -132,7 +151,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   float l_part = 0.f, mu_part = 0.f;  // this lane's half of the row sums
   // log2(e) and 1 when the scale is already in the scores
   const float sl2 = SCALE_IN_Q ? 1.44269504088896340736f : a.scale_log2, c = SCALE_IN_Q ? 1.0f : a.scale;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const op2_t ones = {1.0f, 1.0f};
 
   int koff[NKK];
 #pragma unroll
@@ -214,11 +233,12 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
             for (int r = 0; r < 16; ++r) ABacc[db][r] *= alpha;
         }
       }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      const float m_use = (m_run == -INFINITY ? 0.f : m_run) + kPScaleLog2;
 
-      // p~ = exp2(c log2e s - m); u = p~ * (c ts).  Both rounded to bf16 once;
-      // l and mu are summed from the rounded values.
-      bf16x8_t P[2], U[2];
+      // p~ = exp2(c log2e s - m) (times 2^-8 in fp16); u = p~ * (c ts).  Both
+      // rounded once to the value-product type; l and mu are summed from the
+      // rounded values.
+      op8_t P[2], U[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -231,11 +251,16 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
             u.x = p.x * (TS[r] * c);
             u.y = p.y * (TS[r + 1] * c);
           }
-          const bf16x2_t pb = __builtin_convertvector(p, bf16x2_t);
-          bf16x2_t ub;
-          if constexpr (HAS_TS) ub = __builtin_convertvector(u, bf16x2_t);
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
-          if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+          const op2_t pb = __builtin_convertvector(p, op2_t);
+          op2_t ub;
+          if constexpr (HAS_TS) ub = __builtin_convertvector(u, op2_t);
+          if constexpr (F16) {
+            l_part = __builtin_amdgcn_fdot2(pb, ones, l_part, false);
+            if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2(ub, ones, mu_part, false);
+          } else {
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
+            if constexpr (HAS_TS) mu_part = __builtin_amdgcn_fdot2_f32_bf16(ub, ones, mu_part, false);
+          }
           P[st][t] = pb.x;
           P[st][t + 1] = pb.y;
           if constexpr (HAS_TS) {
@@ -260,12 +285,12 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
             ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
             tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
           }
-          const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          Oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[st], Oacc[db], 0, 0, 0);
-          if constexpr (HAS_TS) ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, U[st], ABacc[db], 0, 0, 0);
+          const op8_t vop = __builtin_bit_cast(op8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+          Oacc[db] = mfma32(vop, P[st], Oacc[db]);
+          if constexpr (HAS_TS) ABacc[db] = mfma32(vop, U[st], ABacc[db]);
           if constexpr (HAS_TKV) {
-            const bf16x8_t tvop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
-            ABacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tvop, P[st], ABacc[db], 0, 0, 0);
+            const op8_t tvop = __builtin_bit_cast(op8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+            ABacc[db] = mfma32(tvop, P[st], ABacc[db]);
           }
         }
       }
@@ -287,6 +312,9 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     // landed and every wave is done with the other buffer, which the next
     // tile's DMA then refills.
     wait_vmcnt<0>();
+    // fp16 value products: this wave's share of the V and tV tiles, converted
+    // before the barrier publishes them
+    if constexpr (F16) bf16_chunks_to_f16<kWavesQ32, D>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
     if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{});
@@ -332,7 +360,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
         }
       }
     if (hi == 0)
-      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + kPScaleLog2 + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

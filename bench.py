@@ -46,13 +46,24 @@ METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak,
 METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_BWD = "masked attention backward TFLOP/s (unmasked FLOPs, 10d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_KV = "KV-cache chunk attention TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
-# What the measured JVP kernel (16-row waves, head_dim 128) is built from.
-KERNEL_SRCS = [os.path.join(ROOT, "attention_jvp_causal_amd", "csrc", n)
-               for n in ("aj_internal.h", "aj_launch.h", "aj_device.h", "attn_jvp_fwd.hip")]
+# What each JVP kernel is built from: its source file and the headers it
+# includes (the 16-row kernel at head_dim 128, the 32-row kernel at 64).
+_CSRC = os.path.join(ROOT, "attention_jvp_causal_amd", "csrc")
+KERNEL_SRCS = {
+    "attn_jvp_fwd.hip": [os.path.join(_CSRC, n) for n in ("aj_tiles.h", "aj_launch.h", "aj_device.h",
+                                                          "attn_jvp_fwd.hip")],
+    "attn_fwd_q32.hip": [os.path.join(ROOT, "include", "attn_jvp.h")] +
+                        [os.path.join(_CSRC, n) for n in ("aj_tiles.h", "aj_launch.h", "aj_device.h",
+                                                          "attn_fwd_q32.hip")],
+}
 
 
-def kernel_sha() -> str:
-    """Hash of the JVP kernel's sources with comments and blank lines removed,
+def kernel_source(head_dim: int) -> str:
+    return "attn_jvp_fwd.hip" if head_dim == 128 else "attn_fwd_q32.hip"
+
+
+def kernel_sha(source: str = "attn_jvp_fwd.hip") -> str:
+    """Hash of a JVP kernel's sources with comments and blank lines removed,
     and of the compiler flags they are built with (include paths aside), so
     that a counter record stays valid across comment-only edits and no
     longer."""
@@ -61,12 +72,13 @@ def kernel_sha() -> str:
     from attention_jvp_causal_amd import build as _build
 
     src = ""
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[source]:
         with open(path) as f:
             src += f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     code = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
-    flags = " ".join(f for f in _build.compile_flags("attn_jvp_fwd.hip") if not f.startswith("-I"))
+    flags = " ".join(f for f in _build.compile_flags(source) if not f.startswith("-I"))
     return hashlib.sha256((code + "\n" + flags).encode()).hexdigest()[:16]
 
 
@@ -96,12 +108,14 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
 def measured_traffic(workload: str):
     """HBM bytes per launch from the rocprofv3 counter runs recorded under
     profiles/, or None if they were taken on a different kernel source."""
+    from attention_jvp_causal_amd.workloads import WORKLOADS
+
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or workload not in WORKLOADS:
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != kernel_sha(kernel_source(WORKLOADS[workload].head_dim)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -119,7 +133,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int
     from attention_jvp_causal_amd.workloads import WORKLOADS
 
     w = WORKLOADS[workload]
-    kname = kernel_name(w.dtype, w.head_dim, False)
+    kname = kernel_name(w.dtype, w.head_dim, False, scale=w.scale)
     kname_sym = kname.split("<")[0]
 
     def per_dispatch(path, counter):
@@ -143,7 +157,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int
     rec = {
         "workload": workload,
         "kernel": kname,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(kernel_source(w.head_dim)),
         "fetch_size_kib_per_dispatch": round(fk, 1),
         "write_size_kib_per_dispatch": round(wk, 1),
         "dispatches_averaged": [nf, nw],

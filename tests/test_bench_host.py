@@ -53,15 +53,20 @@ def test_clock_sampler_without_sysfs_reports_nothing():
     assert c.stop() is None
 
 
-def test_traffic_record_matches_the_kernel_sources():
+def test_traffic_records_match_the_kernel_sources():
     # bench.py reports roofline.traffic only while the counter record was
     # taken on the current kernel sources and flags; a kernel change needs a
-    # new record (bench.py --record-traffic)
-    from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD
+    # new record (bench.py --record-traffic).  The bench workload must have one.
+    import glob
 
-    path = os.path.join(ROOT, "profiles", f"traffic_{BENCH_WORKLOAD}.json")
-    with open(path) as f:
-        rec = json.load(f)
-    assert rec["kernel_sha"] == bench.kernel_sha()
-    assert rec["kernel"] == bench.kernel_name("bf16", 128, False)
-    assert bench.measured_traffic(BENCH_WORKLOAD) == rec["bytes_per_launch"] > 0
+    from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD, WORKLOADS
+
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")))
+    assert os.path.join(ROOT, "profiles", f"traffic_{BENCH_WORKLOAD}.json") in paths
+    for path in paths:
+        with open(path) as f:
+            rec = json.load(f)
+        w = WORKLOADS[rec["workload"]]
+        assert rec["kernel_sha"] == bench.kernel_sha(bench.kernel_source(w.head_dim)), path
+        assert rec["kernel"] == bench.kernel_name(w.dtype, w.head_dim, False, scale=w.scale), path
+        assert bench.measured_traffic(w.name) == rec["bytes_per_launch"] > 0, path

@@ -1,9 +1,9 @@
 """HIP primal masked attention (attn_fwd) vs the fp64 oracle and vs the JVP.
 
-At head_dim 64 attn_fwd runs the JVP kernel's code without the tangent
-products, so its O and lse equal attn_jvp_fwd's bit for bit; at 128 it runs
-32-row waves (a different summation order) and agrees to rounding.  Against
-the oracle's O and lse the usual bf16 tolerances apply.
+attn_fwd rounds p~ to bf16 for its value products; the JVP kernels do so at
+head_dim 128 (16-row waves, a different summation order) and round it to fp16
+at 64.  Either way O and lse agree with the JVP's to rounding.  Against the
+oracle's O and lse the usual bf16 tolerances apply.
 """
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 import attention_jvp_causal_amd as aj
 from attention_jvp_causal_amd.workloads import WORKLOADS, Workload, as_float64, make_inputs
 from oracle import attn_jvp_ref
-from parity_util import TOL, max_abs, oracle_mask, rel_l2, sample_rows, to_np
+from parity_util import TOL, lse_gap_bound, max_abs, oracle_mask, rel_l2, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -25,16 +25,14 @@ def _desc(w):
 
 
 def _same_as_jvp(o, lse, o_j, lse_j, D):
-    if D == 64:
-        assert torch.equal(o, o_j) and torch.equal(lse, lse_j)
-    else:
-        # both round p~ to bf16 before summing l, each against its own running
-        # max: lse agrees to the bf16 rounding of l, O to a few bf16 units
-        do = (o.float() - o_j.float()).abs().max().item()
-        dl = (lse - lse_j).abs().max().item()
-        print(f"[cmp] d128 primal vs jvp: max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
-        assert do <= 2e-2 * max(1.0, o_j.float().abs().max().item())
-        assert dl <= 4e-3
+    # both round p~ (bf16, or fp16 in the d = 64 JVP) before summing l, each
+    # against its own running max: lse agrees to the rounding of l, O to a few
+    # bf16 units
+    do = (o.float() - o_j.float()).abs().max().item()
+    dl = (lse - lse_j).abs().max().item()
+    print(f"[cmp] d{D} primal vs jvp: max|dO| {do:.2e} max|dlse| {dl:.2e} (bound {lse_gap_bound(D):.2e})", flush=True)
+    assert do <= 2e-2 * max(1.0, o_j.float().abs().max().item())
+    assert dl <= lse_gap_bound(D)
 
 
 def _check_primal(w, got, ref, label):

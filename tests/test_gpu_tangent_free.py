@@ -5,9 +5,8 @@ When the declared tangents are zero, the skipped products only ever add exact
 zeros.  Query tiles that keep some tangent work run the JVP kernel's variant
 instance: their O and lse are bitwise those of the plain descriptor's run.
 Query tiles left with only primal work run the primal forward kernel (tO = 0
-written): bitwise equal at d = 64, where it is the JVP kernel's own code, and
-equal to rounding at d = 128 (32-row instead of 16-row waves, as for
-attn_fwd).  tO is equal in value everywhere; against the oracle the usual
+written): equal to rounding, as for attn_fwd (at d = 128 32-row instead of
+16-row waves, at d = 64 p~ in bf16 instead of the JVP's fp16).  tO is equal in value everywhere; against the oracle the usual
 tolerances apply.
 """
 import numpy as np
@@ -17,7 +16,7 @@ import torch
 import attention_jvp_causal_amd as aj
 from attention_jvp_causal_amd.workloads import WORKLOADS, Workload, as_float64, make_inputs
 from oracle import RectMask, attn_jvp_ref
-from parity_util import compare, oracle_mask, sample_rows, to_np
+from parity_util import compare, lse_gap_bound, oracle_mask, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -53,14 +52,11 @@ def _same_as_plain(fast, plain, label, desc):
         return
     o, o_p = fast[0][:, :, pr], plain[0][:, :, pr]
     lse, lse_p = fast[2][:, :, pr], plain[2][:, :, pr]
-    if desc.head_dim == 64:
-        assert torch.equal(o, o_p) and torch.equal(lse, lse_p), f"{label}: primal rows differ at d = 64"
-    else:
-        do = (o.float() - o_p.float()).abs().max().item()
-        dl = (lse - lse_p).abs().max().item()
-        print(f"[cmp] {label} primal rows: max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
-        assert do <= 2e-2 * max(1.0, o_p.float().abs().max().item()), f"{label}: O on the primal rows"
-        assert dl <= 4e-3, f"{label}: lse on the primal rows"
+    do = (o.float() - o_p.float()).abs().max().item()
+    dl = (lse - lse_p).abs().max().item()
+    print(f"[cmp] {label} primal rows: max|dO| {do:.2e} max|dlse| {dl:.2e}", flush=True)
+    assert do <= 2e-2 * max(1.0, o_p.float().abs().max().item()), f"{label}: O on the primal rows"
+    assert dl <= lse_gap_bound(desc.head_dim), f"{label}: lse on the primal rows"
 
 
 def _layout_desc(w):
