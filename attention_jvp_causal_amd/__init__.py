@@ -98,11 +98,12 @@ def lib() -> ctypes.CDLL:
     L.attn_jvp_mask_desc_from_rects_kv.argtypes = [i32, i32, P, i32, i32, i32, ctypes.POINTER(pdesc)]
     L.attn_jvp_mask_desc_col_bits.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
     L.attn_jvp_mask_desc_upload.argtypes = [pdesc, i32]
+    L.attn_bwd_noalloc.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
     for fn in ("attn_jvp_mask_desc_build", "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_stats",
                "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
                "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
                "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits", "attn_fwd_kv",
-               "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_mask_desc_upload"):
+               "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_mask_desc_upload", "attn_bwd_noalloc"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -460,9 +461,36 @@ def attn_bwd(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = Non
     return dq, dk, dv, delta
 
 
+def attn_bwd_noalloc(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
+                     out: Optional[Tuple] = None, stream=None):
+    """attn_bwd for callers that cannot allocate device memory: D is kept in the
+    library's per-GPU array (B * H * L <= 4,194,304; calls that overlap on one
+    GPU race).  Returns (dq, dk, dv); ``out`` may pass preallocated (dq, dk, dv)
+    so that the call allocates nothing at all."""
+    import torch
+
+    ins = (q, k, v, o, dout)
+    B, H, L, D = q.shape
+    if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on the inputs' device")
+    if out is None:
+        sh, (dq, dk, dv), _, scale = _prepare(ins, out_dtype, scale, None, 3)
+    else:
+        # _prepare's out carries an lse slot; pass the input lse there (only checked)
+        sh, (dq, dk, dv), _, scale = _prepare(ins, out_dtype, scale, tuple(out) + (lse,), 3)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_noalloc(ctypes.byref(sh), *(t.data_ptr() for t in ins), lse.data_ptr(), mask.handle,
+                                    scale, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_bwd_noalloc")
+    return dq, dk, dv
+
+
 __all__ = [
     "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_ENOTLOADED", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
     "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
-    "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_fwd", "attn_fwd_kv", "attn_bwd", "LIB_PATH",
+    "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_noalloc",
+    "LIB_PATH",
 ]

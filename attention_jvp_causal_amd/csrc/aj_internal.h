@@ -71,4 +71,13 @@ int32_t build_from_rects(int32_t q_len, int32_t kv_len, const int32_t* rects, in
                          int32_t dtype, const int32_t* tfree, int32_t n_tfree, aj_mask_desc** out);
 // Expands a frame-level layout into disjoint rectangles.
 int32_t layout_rects(const aj_mask_spec* spec, int32_t seq_len, std::vector<int32_t>* rects);
+
+// Capacity (floats) of the per-GPU array that holds D for attn_bwd_noalloc:
+// B * H * L of a call may not exceed it (16 MiB).
+constexpr int64_t kBwdScratchFloats = int64_t(1) << 22;
+
+// Device address of that array on the current device (attn_bwd.hip: looked
+// up once per device with hipGetSymbolAddress, then cached); allocates
+// nothing.  Returns an aj_status.
+int bwd_scratch(float** out);
 }  // namespace aj

@@ -31,10 +31,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/attn_jvp.h"
 #include "aj_device.h"
+#include "aj_internal.h"
 #include "aj_launch.h"
 
 namespace aj {
@@ -508,6 +510,31 @@ int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream) {
     else launch_bwd_d<64, false>(a, stream);
   }
   return hipGetLastError() == hipSuccess ? AJ_OK : AJ_EHIP;
+}
+
+// Row statistic D of the gradient kernels for attn_bwd_noalloc, which takes
+// no workspace argument: written by the dQ kernel, read by the dK / dV kernel
+// of the same call.  One array per GPU for the life of the process; every
+// attn_bwd_noalloc call on a GPU uses it, so calls that overlap on one GPU
+// race.  Nothing in it needs clearing: each call writes every entry it reads
+// before reading it.  Host code never names the array itself (its host-side
+// name is not a device address): it uses the address bwd_scratch returns.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+int bwd_scratch(float** out) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AJ_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return AJ_ENOTSUP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AJ_EHIP;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return AJ_OK;
 }
 
 }  // namespace aj

@@ -257,6 +257,9 @@ int32_t attn_jvp_mask_desc_upload(aj_mask_desc* d, int32_t device) {
   } catch (const std::bad_alloc&) {
     st = AJ_ENOMEM;
   }
+  // set-up of the device for attn_bwd_noalloc: the address of its array
+  float* scratch_addr = nullptr;
+  if (st == AJ_OK) st = aj::bwd_scratch(&scratch_addr);
   if (cur != device) (void)hipSetDevice(cur);
   return st;
 }
@@ -388,22 +391,32 @@ int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v,
                         static_cast<hipStream_t>(stream));
 }
 
-int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, const aj_mask_desc* mask, float scale, void* dq, void* dk, void* dv,
-                 float* delta, void* stream) {
+// The gradient entry points: attn_bwd with the caller's delta, attn_bwd_noalloc
+// (delta == nullptr) with the library's per-GPU array.
+static int32_t bwd_entry(const aj_shape* s, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
+                         void* dk, void* dv, float* delta, void* stream) {
   // checks of this entry point first: nothing may reach the device before all pass
   if (!s || !mask) return AJ_EINVAL;
   if (!lse || !aligned16(lse)) return AJ_EINVAL;
   if (s->in_dtype != AJ_BF16) return AJ_ENOTSUP;
   if (mask->kv_len != mask->seq_len) return AJ_EMASK;
+  const bool own_delta = delta == nullptr;
+  if (own_delta && (s->batch < 1 || s->heads < 1 || s->seq_len < 1 ||
+                    int64_t(s->batch) * s->heads * s->seq_len > aj::kBwdScratchFloats))
+    return AJ_EINVAL;
   const void* ins[5] = {q, k, v, o, dout};
   const void* outs[4] = {dq, dk, dv, delta};
   aj::FwdArgs f;
-  int32_t st = prepare(s, ins, 5, outs, 4, mask, scale, &f);
+  int32_t st = prepare(s, ins, 5, outs, own_delta ? 3 : 4, mask, scale, &f);
   if (st != AJ_OK) return st;
   const DeviceTables* t = nullptr;
   st = device_tables(mask, &t);
   if (st != AJ_OK) return st;
+  if (own_delta) {
+    st = aj::bwd_scratch(&delta);
+    if (st != AJ_OK) return st;
+  }
   aj::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
   a.lse = lse; a.delta = delta;
@@ -418,6 +431,19 @@ int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v,
   a.rows = t->rows;
   a.cols = t->cols;
   return aj::launch_bwd(a, s->out_dtype, s->head_dim, static_cast<hipStream_t>(stream));
+}
+
+int32_t attn_bwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, const aj_mask_desc* mask, float scale, void* dq, void* dk, void* dv,
+                 float* delta, void* stream) {
+  if (!delta) return AJ_EINVAL;
+  return bwd_entry(s, q, k, v, o, dout, lse, mask, scale, dq, dk, dv, delta, stream);
+}
+
+int32_t attn_bwd_noalloc(const aj_shape* s, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
+                         void* dk, void* dv, void* stream) {
+  return bwd_entry(s, q, k, v, o, dout, lse, mask, scale, dq, dk, dv, nullptr, stream);
 }
 
 int32_t attn_fwd_kv(const aj_kv_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,

@@ -307,6 +307,22 @@ int32_t attn_bwd(const aj_shape* shape, const void* q, const void* k, const void
                  const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
                  void* dk, void* dv, float* delta, void* stream);
 
+/* attn_bwd without the delta workspace, for callers that cannot allocate
+ * device memory (code under HIP-graph capture, tight training loops,
+ * harnesses that forbid hipMalloc): D lives in an array the library keeps in
+ * device memory, one per GPU for the life of the process (16 MiB).  Same
+ * operation, kernels, results (bit for bit), checks and errors as attn_bwd,
+ * minus the delta argument; in addition B * H * L must not exceed 4,194,304
+ * (AJ_EINVAL otherwise, before any device work).  Allocates nothing: the
+ * array's address is looked up once per device (at attn_jvp_mask_desc_upload
+ * or, failing that, at the first call on the device).  Every call on a GPU
+ * shares that GPU's array: calls that may overlap in time on one GPU (other
+ * streams, other threads) race and give wrong gradients; calls in one
+ * stream's order are safe. */
+int32_t attn_bwd_noalloc(const aj_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const aj_mask_desc* mask, float scale, void* dq,
+                         void* dk, void* dv, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -280,3 +280,23 @@ def test_upload_rejects_bad_arguments():
         d2 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16")
         assert d2.stats()["seq_len"] == 64
 
+
+def test_noalloc_gradients_reject_sizes_beyond_the_array():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; checked on the host only")
+    # B * H * L = 1 * 64 * 65600 > 4,194,304: refused before any device work
+    d = aj.attn_jvp_mask_desc_build("full", 1, 65600, 1, head_dim=64, dtype="bf16")
+    sh = _shape(B=1, H=64, L=65600, D=64)
+    p = [ctypes.c_void_p(FAKE)] * 8
+    st = aj.lib().attn_bwd_noalloc(ctypes.byref(sh), *p[:5], ctypes.c_void_p(FAKE), d.handle, ctypes.c_float(0.125),
+                                   *p[5:8], None)
+    assert st == aj.AJ_EINVAL
+    # within the limit the same call gets as far as the device (none here)
+    d2 = aj.attn_jvp_mask_desc_build("full", 1, 64, 1, head_dim=64, dtype="bf16")
+    sh2 = _shape(B=1, H=2, L=64, D=64)
+    st = aj.lib().attn_bwd_noalloc(ctypes.byref(sh2), *p[:5], ctypes.c_void_p(FAKE), d2.handle, ctypes.c_float(0.125),
+                                   *p[5:8], None)
+    assert st == aj.AJ_EHIP
+    # attn_bwd itself needs its delta argument
+    assert _bwd(sh2, d2.handle, delta=None) == aj.AJ_EINVAL
