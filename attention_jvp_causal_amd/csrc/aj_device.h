@@ -43,13 +43,29 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_
 // swz(r) = 4 ((r >> 2) ^ 2 ((r >> 1) & 1)) + 2 (r & 1) meets both.  These lane
 // groupings were inferred from the LDS bank-conflict counter: it reads 0 for
 // this swizzle in the kernels, and about 4 stalled cycles per b128 read for
-// 2 (r % 8) + (r / 8) % 2, which meets only the second condition.  D = 64
-// keeps 2 ((r / 2) % 4) + (r / 8) % 2.
+// 2 (r % 8) + (r / 8) % 2, which meets only the second condition.
+//
+// At D = 64 a row is 128 bytes and two rows share one 256-byte line of the
+// banks: 16-byte position p of the row in LDS slot s lies in bank unit
+// 8 (s % 2) + p.  Stored in place, the rows k, k+4, k+8, k+12 that one group
+// of a row read serves all have the parity of k, so their 16 chunks meet 8
+// units (a 2-way conflict on every b128 read; the counter read 5.9e8 per
+// launch in the d = 64 dK / dV kernel).  Tile row r is therefore stored in
+// slot slot_q16(r) = r with bits 0 and 2 swapped, which puts two of those rows
+// in each half line, and swz(r) = 2 (r % 4) ^ 4 ((r / 8) % 2) gives the two
+// rows of a half line different bit 2; the eight rows of a transpose read
+// still take four different swz(r) >> 1 in each half line.
 template <int D>
 __device__ __forceinline__ int swz_q16(int r) {
   static_assert(D == 64 || D == 128, "head_dim");
   return D == 128 ? (((((r >> 2) ^ (((r >> 1) & 1) << 1)) & 3) << 2) | ((r & 1) << 1))
-                  : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+                  : ((((r & 3) << 1) ^ ((r & 8) >> 1)) & 7);
+}
+// LDS row slot of tile row r (an involution; the identity at D = 128)
+template <int D>
+__device__ __forceinline__ int slot_q16(int r) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  return D == 128 ? r : ((r & ~5) | ((r & 1) << 2) | ((r >> 2) & 1));
 }
 template <int D>
 __device__ __forceinline__ int swz_q32(int r) {
@@ -98,22 +114,37 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Per-lane byte offsets (inside one key tile of one tensor) of the 16-byte
 // chunks this lane moves.  Wave instruction i fills 1 KB block blk = wave +
-// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. row r = chunk /
-// CH at swizzled position p, so it fetches logical chunk p ^ swz(r) of row r.
+// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. slot s = chunk /
+// CH at swizzled position p; the slot holds tile row r = slot(s) (slot is an
+// involution, the identity unless given), so the lane fetches logical chunk
+// p ^ swz(r) of row r.
 template <int NW, int D>
 struct TileLoadPlan {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int NI = (BN * CH) / (64 * NW);   // wave instructions per tensor
   uint32_t voff[NI];
-  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int)) {
+  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int),
+                                          int (*slot)(int) = nullptr) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int ci = (wave + NW * i) * 64 + lane;
-      const int r = ci / CH, p = ci % CH;
+      const int s = ci / CH, p = ci % CH;
+      const int r = slot ? (s & ~15) | slot(s & 15) : s;
       voff[i] = uint32_t(r * sl * 2 + ((p ^ swz(r)) << 4));
     }
   }
 };
+
+// A value every lane of the wave holds alike, moved to a scalar register.  The
+// tile-map walk (task, entry offsets, entries) is wave-uniform; held in scalar
+// registers it lets the compiler do the key-tile DMA's address arithmetic on
+// the scalar unit, instead of in vector registers followed by readfirstlane
+// and the wait states that a scalar read of a vector-written value needs.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ Entry load_entry(const Entry* p) {
+  const Entry e = *p;
+  return Entry{wave_uniform(e.kt0), wave_uniform(e.kt1), wave_uniform(e.pidx), wave_uniform(e.flags)};
+}
 
 // Workgroup index -> (task rank, flattened head b * H + h).  The B * H heads
 // are taken in groups of G: all workgroups of one group come before those of
@@ -134,10 +165,15 @@ __device__ __forceinline__ TaskCoord task_coord(int idx, int n_tasks, int BH, in
   return {rank, grp * G + (rem - rank * gsz)};
 }
 
-// DMA of rows [row0, row0 + BN) of two [L, D] tensors into dst[0] and
-// dst[1] (rows past L read as zero).
+// LDS addresses below are byte addresses in the workgroup's LDS: the
+// kernels take the address of their LDS struct once (lds_addr) and add the
+// struct's constant member offsets, so that with the wave index and the tile
+// index in scalar registers the DMA addresses are scalar arithmetic.
+
+// DMA of rows [row0, row0 + BN) of two [L, D] tensors into the two tiles
+// starting at LDS byte address lds_buf (rows past L read as zero).
 template <int NW, int D>
-__device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
+__device__ __forceinline__ void issue_pair_loads(uint32_t lds_buf, const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* s0, const uint16_t* s1, int64_t sl, int row0, int L,
                                                  int wave) {
   const int nrec = int((int64_t)min(L - row0, BN) * sl * 2);
@@ -145,15 +181,16 @@ __device__ __forceinline__ void issue_pair_loads(uint16_t (*dst)[BN * D], const 
   const i32x4_t r1 = make_rsrc(s1 + (int64_t)row0 * sl, nrec);
 #pragma unroll
   for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[0] + (wave + NW * i) * 512), plan.voff[i], r0);
+    lds_dma_16(lds_buf + (wave + NW * i) * 1024, plan.voff[i], r0);
 #pragma unroll
   for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-    lds_dma_16(lds_addr(dst[1] + (wave + NW * i) * 512), plan.voff[i], r1);
+    lds_dma_16(lds_buf + BN * D * 2 + (wave + NW * i) * 1024, plan.voff[i], r1);
 }
 
-// Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx.
-__device__ __forceinline__ void issue_bits_load(uint64_t* dst, const uint64_t* bits, int pidx, int lane) {
-  lds_dma_16(lds_addr(dst), uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));
+// Wave 0 loads the 128 per-row key bitmasks (1 KB) of partial tile pidx to
+// LDS byte address lds_bits.
+__device__ __forceinline__ void issue_bits_load(uint32_t lds_bits, const uint64_t* bits, int pidx, int lane) {
+  lds_dma_16(lds_bits, uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -190,7 +227,7 @@ __device__ __forceinline__ float row4_sum(float x) {
 // its max grows by more than 2^8 (log2 units).
 constexpr float kLazyRescaleLog2 = 8.0f;
 
-// Rewrites, in place, the 16-byte chunks of two key tiles (V and tV) that this
+// Rewrites, in place, the 16-byte chunks of NTEN key tiles (V, then tV) that this
 // wave's lanes brought in by DMA (issue_tile_loads: wave instruction i of lane
 // l fills chunk (wave + NW i) * 64 + l of each tensor tile) from bf16 to fp16.
 // Every bf16 value of magnitude in [2^-14, 65504] is an fp16 value, so the
@@ -198,11 +235,11 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 // resolution (2^-24) and larger ones saturate to 65504 (round toward zero).
 // Called after the wave's own DMA has landed (vmcnt 0) and before the barrier
 // that publishes the buffer, so no other wave reads these chunks meanwhile.
-template <int NW, int D>
+template <int NW, int D, int NTEN>
 __device__ __forceinline__ void bf16_chunks_to_f16(uint16_t* t0, uint16_t* t1, int wave, int lane) {
   constexpr int NI = TileLoadPlan<NW, D>::NI;
 #pragma unroll
-  for (int i = 0; i < 2 * NI; ++i) {
+  for (int i = 0; i < NTEN * NI; ++i) {
     uint16_t* p = (i < NI ? t0 : t1) + (wave + NW * (i % NI)) * 512 + 8 * lane;
     const u32x4_t x = *(const u32x4_t*)p;
     u32x4_t y;
@@ -225,13 +262,18 @@ struct Bf16Lds {
   uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
   // LDS slot of tensor t in {0: K, 1: tK, 2: V, 3: tV}
   static constexpr __device__ int slot(int t) { return NT == 4 ? t : t / 2; }
+  // byte offsets of t[b][0] and bits[b] from the start of the struct
+  static constexpr __device__ uint32_t t_off(int b) { return uint32_t(b) * NT * TILE * 2; }
+  static constexpr __device__ uint32_t bits_off(int b) { return 2u * NT * TILE * 2 + uint32_t(b) * BM * 8; }
 };
 // Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
 // when TANG, into one LDS buffer.  Returns immediately; completion is tracked
 // by vmcnt.  The buffer resource ends at row L, so rows past the end read as
 // zero.
+// lds_buf: LDS byte address of the buffer's first tensor tile; tensor slot s
+// starts BN * D * 2 * s bytes further on.
 template <int NW, int D, bool TANG, int NT>
-__device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const TileLoadPlan<NW, D>& plan,
+__device__ __forceinline__ void issue_tile_loads(uint32_t lds_buf, const TileLoadPlan<NW, D>& plan,
                                                  const uint16_t* const src[4], int64_t sl, int key0, int L,
                                                  int wave) {
   const int nrec = int((int64_t)min(L - key0, BN) * sl * 2);
@@ -239,9 +281,9 @@ __device__ __forceinline__ void issue_tile_loads(uint16_t (*dst)[BN * D], const 
   for (int t = 0; t < 4; ++t) {
     if (!TANG && (t & 1)) continue;  // tK, tV
     const i32x4_t rs = make_rsrc(src[t] + (int64_t)key0 * sl, nrec);
+    const uint32_t tile = lds_buf + uint32_t(NT == 4 ? t : t / 2) * BN * D * 2;
 #pragma unroll
-    for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i)
-      lds_dma_16(lds_addr(dst[NT == 4 ? t : t / 2] + (wave + NW * i) * 512), plan.voff[i], rs);
+    for (int i = 0; i < TileLoadPlan<NW, D>::NI; ++i) lds_dma_16(tile + (wave + NW * i) * 1024, plan.voff[i], rs);
   }
 }
 

@@ -50,14 +50,23 @@ struct BwdLds {
   uint16_t t[2][2][TILE];              // [buffer][(K, V) for dQ | (Q, dO) for dK, dV]
   uint64_t bits[2][BM];                // per-row bitmask of a partial tile
   float rowv[2][2][BN];                // [buffer][lse, D] of the 64 streamed queries
+  // byte offsets of t[b][0], bits[b] and rowv[b][i] from the start of the struct
+  static constexpr __device__ uint32_t t_off(int b) { return uint32_t(b) * 2 * TILE * 2; }
+  static constexpr __device__ uint32_t bits_off(int b) { return 4u * TILE * 2 + uint32_t(b) * BM * 8; }
+  static constexpr __device__ uint32_t rowv_off(int b, int i) {
+    return 4u * TILE * 2 + 2u * BM * 8 + uint32_t(2 * b + i) * BN * 4;
+  }
 };
 
 // K and V tiles only (the 32-row dQ kernel): 66 KB at d = 128 (two workgroups
 // per CU), 34 KB at d = 64 (three).
 template <int D>
 struct KvLds {
-  uint16_t t[2][2][BN * D];  // [buffer][K, V]
+  static constexpr int TILE = BN * D;
+  uint16_t t[2][2][TILE];  // [buffer][K, V]
   uint64_t bits[2][BM];
+  static constexpr __device__ uint32_t t_off(int b) { return uint32_t(b) * 2 * TILE * 2; }
+  static constexpr __device__ uint32_t bits_off(int b) { return 4u * TILE * 2 + uint32_t(b) * BM * 8; }
 };
 
 // One direct buffer -> LDS load of 4 bytes per lane (lane l's dword lands at
@@ -95,14 +104,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqW
 void attn_bwd_dq32_kernel(BwdArgs a) {
   constexpr int NKK = D / 16;  // MFMA k-steps over d for S^T and dP^T
   constexpr int NDB = D / 32;  // 32-row blocks of d for dQ^T
-  __shared__ __attribute__((aligned(1024))) KvLds<D> s;
+  using Lds = KvLds<D>;
+  __shared__ __attribute__((aligned(1024))) Lds s;
+  static_assert(offsetof(Lds, bits) == Lds::bits_off(0), "LDS layout");
+  const uint32_t lds0 = lds_addr(&s);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_uniform(tid >> 6), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
   const TaskCoord tc = task_coord(blockIdx.x, a.n_row_tasks, BH, a.head_group);
   const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.rows.tasks[rank];
+  const int qt = wave_uniform(a.rows.tasks[rank]);
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const int64_t bhL = (int64_t)bh * L;
@@ -134,14 +146,14 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
 
   const TileLoadPlan<kDqWaves32, D> plan(a.isl, wave, lane, swz_q32<D>);
   auto prefetch = [&](int b, const Entry& x, int kti) {
-    issue_pair_loads<kDqWaves32, D>(s.t[b], plan, Kg, Vg, a.isl, kti * BN, L, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.rows.bits, x.pidx, lane);
+    issue_pair_loads<kDqWaves32, D>(lds0 + Lds::t_off(b), plan, Kg, Vg, a.isl, kti * BN, L, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.rows.bits, x.pidx, lane);
   };
-  const int e0 = a.rows.qt_off[qt], e1 = a.rows.qt_off[qt + 1];
+  const int e0 = wave_uniform(a.rows.qt_off[qt]), e1 = wave_uniform(a.rows.qt_off[qt + 1]);
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
-    en = a.rows.entries[e];
+    en = load_entry(a.rows.entries + e);
     kt = en.kt0;
     prefetch(0, en, kt);
   }
@@ -175,7 +187,7 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
     if (kt_n >= en.kt1) {
       e_n = e + 1;
       if (e_n < e1) {
-        en_n = a.rows.entries[e_n];
+        en_n = load_entry(a.rows.entries + e_n);
         kt_n = en_n.kt0;
       }
     }
@@ -282,14 +294,17 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NDB = D / 16;
   constexpr int NW = dkdv_waves<D>();
   constexpr int PARTS = BM / (16 * NW);  // workgroups per column-map tile
-  __shared__ __attribute__((aligned(1024))) BwdLds<D> s;
+  using Lds = BwdLds<D>;
+  __shared__ __attribute__((aligned(1024))) Lds s;
+  static_assert(offsetof(Lds, bits) == Lds::bits_off(0) && offsetof(Lds, rowv) == Lds::rowv_off(0, 0), "LDS layout");
+  const uint32_t lds0 = lds_addr(&s);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = wave_uniform(tid >> 6), lane = tid & 63, j16 = lane & 15, g = lane >> 4;
   const int BH = a.B * a.H;
   const TaskCoord tc = task_coord(blockIdx.x, a.n_col_tasks * PARTS, BH, a.head_group);
   const int rank = tc.rank / PARTS, kpart = tc.rank - rank * PARTS, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int ktile = a.cols.tasks[rank];
+  const int ktile = wave_uniform(a.cols.tasks[rank]);
   const int key_in_tile = kpart * 16 * NW + wave * 16 + j16;  // row of the tile's bitmask
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
@@ -313,24 +328,24 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vmcnt<0>();
 
-  const TileLoadPlan<NW, D> plan(a.isl, wave, lane, swz_q16<D>);
+  const TileLoadPlan<NW, D> plan(a.isl, wave, lane, swz_q16<D>, slot_q16<D>);
   // Q, dO rows of query tile qti; wave 1 brings their lse and D, wave 0 the
   // key bitmasks of a partial tile
   auto prefetch = [&](int b, const Entry& x, int qti) {
     const int row0 = qti * BN;
-    issue_pair_loads<NW, D>(s.t[b], plan, Qg, dOg, a.isl, row0, L, wave);
+    issue_pair_loads<NW, D>(lds0 + Lds::t_off(b), plan, Qg, dOg, a.isl, row0, L, wave);
     if (wave == 1) {
       const int nrec = min(L - row0, BN) * 4;
-      lds_dma_4(lds_addr(s.rowv[b][0]), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
-      lds_dma_4(lds_addr(s.rowv[b][1]), uint32_t(lane) * 4u, make_rsrc(a.delta + bhL + row0, nrec));
+      lds_dma_4(lds0 + Lds::rowv_off(b, 0), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
+      lds_dma_4(lds0 + Lds::rowv_off(b, 1), uint32_t(lane) * 4u, make_rsrc(a.delta + bhL + row0, nrec));
     }
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.cols.bits, x.pidx, lane);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.cols.bits, x.pidx, lane);
   };
-  const int e0 = a.cols.qt_off[ktile], e1 = a.cols.qt_off[ktile + 1];
+  const int e0 = wave_uniform(a.cols.qt_off[ktile]), e1 = wave_uniform(a.cols.qt_off[ktile + 1]);
   int e = e0, qtl = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
-    en = a.cols.entries[e];
+    en = load_entry(a.cols.entries + e);
     qtl = en.kt0;
     prefetch(0, en, qtl);
   }
@@ -344,15 +359,15 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   int koff[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = slot_q16<D>(j16) * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
   const int vrow = 4 * g + (j16 >> 2);
-  // The second read of a pair is 16 rows further on, at the same swizzle
-  // (swz_q16 depends on the row mod 16): a constant offset of 16 D.
+  // The second read of a pair is 16 rows further on, at the same slot and
+  // swizzle (both depend on the row mod 16): a constant offset of 16 D.
   int voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int chunk = 2 * db + ((j16 & 3) >> 1);
-    voff[db] = vrow * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
+    voff[db] = slot_q16<D>(vrow) * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
   }
 
   int buf = 0;
@@ -362,7 +377,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     if (qt_n >= en.kt1) {
       e_n = e + 1;
       if (e_n < e1) {
-        en_n = a.cols.entries[e_n];
+        en_n = load_entry(a.cols.entries + e_n);
         qt_n = en_n.kt0;
       }
     }

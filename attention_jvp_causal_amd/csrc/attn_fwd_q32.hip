@@ -58,7 +58,12 @@ __device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
 template <int D, bool JVP>
 constexpr int q32_waves_per_simd() { return D == 64 && !JVP ? 3 : 2; }
 
-template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false>
+// VARIANTS (JVP only): the descriptor declares tangent-free tokens; tiles whose
+// keys carry no tangent skip the tK and tV DMA, reads and products, the others
+// run them.  Tiles where neither queries nor keys carry tangents take the same
+// keys-tangent-free path: their tQ is zero, so their score tangents and u are
+// exact zeros.
+template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false, bool VARIANTS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32),
                           amdgpu_waves_per_eu(q32_waves_per_simd<D, JVP>(), q32_waves_per_simd<D, JVP>())))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
@@ -78,13 +83,15 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   typedef std::conditional_t<F16, f16x2_t, bf16x2_t> op2_t;
   constexpr float kPScaleLog2 = F16 ? 8.0f : 0.0f;  // p~ is stored as p~ 2^-kPScaleLog2
   __shared__ __attribute__((aligned(1024))) Lds s;
+  static_assert(offsetof(Lds, bits) == Lds::bits_off(0), "LDS layout");
+  const uint32_t lds0 = lds_addr(&s);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_uniform(tid >> 6), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
   const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
   const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.tasks[rank];
+  const int qt = wave_uniform(a.tasks[rank]);
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const int64_t kv_off = bb * a.ksb + hh * a.ksh;
@@ -95,25 +102,21 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   const int q_row = qt * BM + wave * 32 + l32;
 
   const TileLoadPlan<kWavesQ32, D> plan(a.ksl, wave, lane, swz_q32<D>);
-  // At d = 64 the tangent-free variants are not built (three copies of the
-  // tile code do not fit the register budget of two workgroups per CU): every
-  // tile runs the general code, which is exact when the declared tangents are
-  // zero.
+  // DMA of key tile kti of entry x (tK and tV only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
-    (void)x.flags;
-    if (JVP)
-      issue_tile_loads<kWavesQ32, D, true, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
+    if (JVP && (!VARIANTS || x.flags == kTileJvp))
+      issue_tile_loads<kWavesQ32, D, true, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
-      issue_tile_loads<kWavesQ32, D, false, NT>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
+      issue_tile_loads<kWavesQ32, D, false, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.bits, x.pidx, lane);
   };
 
   // first key tile in flight before the prologue
-  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  const int e0 = wave_uniform(a.qt_off[qt]), e1 = wave_uniform(a.qt_off[qt + 1]);
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
-    en = a.entries[e];
+    en = load_entry(a.entries + e);
     kt = en.kt0;
     prefetch(0, en, kt);
   }
@@ -171,10 +174,15 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   int buf = 0;
 
   // One 64-key tile of the variant VAR (which tangents the tile carries).
-  auto tile = [&](auto var_tag) __attribute__((always_inline)) {
+  // tkv_rt: the tile carries tK and tV (wave-uniform; false only for the
+  // keys-tangent-free tiles of a VARIANTS instance).  One code with branches
+  // around the tK and tV work rather than a second copy of the tile code: two
+  // copies need more than the 256 registers of two workgroups per CU.
+  auto tile = [&](auto var_tag, bool tkv_rt) __attribute__((always_inline)) {
     constexpr int VAR = decltype(var_tag)::value;
     constexpr bool HAS_TS = JVP && VAR != kTileAllFree;  // score tangent nonzero
-    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV tiles present
+    constexpr bool HAS_TKV = JVP && VAR == kTileJvp;     // tK and tV products built
+    const bool tkv = HAS_TKV && tkv_rt;
     const uint64_t bits = en.pidx >= 0 ? s.bits[buf][wave * 32 + l32] : ~0ull;
     const uint16_t* Kt = s.t[buf][Lds::slot(0)];
     const uint16_t* tKt = s.t[buf][Lds::slot(1)];
@@ -192,9 +200,13 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
         const int off = kb * 32 * D + koff[kk];
         const bf16x8_t kop = as_bf16x8(*(const u32x4_t*)(Kt + off));
         bf16x8_t tkop;
-        if constexpr (HAS_TKV) tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, Qr[kk], S, 0, 0, 0);
-        if constexpr (HAS_TKV) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
+        if constexpr (HAS_TKV) {
+          if (tkv) {
+            tkop = as_bf16x8(*(const u32x4_t*)(tKt + off));
+            TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkop, Qr[kk], TS, 0, 0, 0);
+          }
+        }
         if constexpr (HAS_TS) TS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, tQr[kk], TS, 0, 0, 0);
       }
       // lane holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of its query row
@@ -280,17 +292,16 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
           const int off_b = (kb * 32 + 16 * st) * D + voff[1][db];
           const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_a));
           const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Vt + off_b));
-          s16x4_t ta, tb;
-          if constexpr (HAS_TKV) {
-            ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
-            tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
-          }
           const op8_t vop = __builtin_bit_cast(op8_t, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
           Oacc[db] = mfma32(vop, P[st], Oacc[db]);
           if constexpr (HAS_TS) ABacc[db] = mfma32(vop, U[st], ABacc[db]);
           if constexpr (HAS_TKV) {
-            const op8_t tvop = __builtin_bit_cast(op8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
-            ABacc[db] = mfma32(tvop, P[st], ABacc[db]);
+            if (tkv) {
+              const s16x4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_a));
+              const s16x4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tVt + off_b));
+              const op8_t tvop = __builtin_bit_cast(op8_t, __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7));
+              ABacc[db] = mfma32(tvop, P[st], ABacc[db]);
+            }
           }
         }
       }
@@ -304,7 +315,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     if (kt_n >= en.kt1) {
       e_n = e + 1;
       if (e_n < e1) {
-        en_n = a.entries[e_n];
+        en_n = load_entry(a.entries + e_n);
         kt_n = en_n.kt0;
       }
     }
@@ -314,11 +325,16 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     // fp16 value products: this wave's share of the V and tV tiles, converted
     // before the barrier publishes them
-    if constexpr (F16) bf16_chunks_to_f16<kWavesQ32, D>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
+    if constexpr (F16) {
+      if (!VARIANTS || en.flags == kTileJvp)
+        bf16_chunks_to_f16<kWavesQ32, D, 2>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
+      else
+        bf16_chunks_to_f16<kWavesQ32, D, 1>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
+    }
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
-    if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{});
-    else tile(std::integral_constant<int, kTileJvp>{});
+    if constexpr (!JVP) tile(std::integral_constant<int, kTileAllFree>{}, false);
+    else tile(std::integral_constant<int, kTileJvp>{}, !VARIANTS || en.flags == kTileJvp);
     e = e_n;
     kt = kt_n;
     en = en_n;
@@ -414,7 +430,7 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
   const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
   const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.tasks[rank];
+  const int qt = wave_uniform(a.tasks[rank]);
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const float* __restrict__ Qg = (const float*)a.q + in_off;
@@ -442,7 +458,7 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_part = 0.f, mu_part = 0.f;
   const float sl2 = a.scale_log2, c = a.scale;
 
-  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  const int e0 = wave_uniform(a.qt_off[qt]), e1 = wave_uniform(a.qt_off[qt + 1]);
   for (int e = e0; e < e1; ++e) {
     const Entry en = a.entries[e];
     const uint64_t bits = en.pidx >= 0 ? a.bits[(int64_t)en.pidx * BM + wave * 32 + l32] : ~0ull;
@@ -565,13 +581,15 @@ static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid,
     const bool pow2 = a.scale > 0.f && a.scale <= 1.f && std::frexp(a.scale, &e2) == 0.5f;
     if constexpr (JVP) {
       if (pow2) {
-        if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true>), grid, b32, 0, stream, a);
-        else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, true>), grid, b32, 0, stream, a);
+        if (out_f32)
+          hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true, VARIANTS>), grid, b32, 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, VARIANTS>), grid, b32, 0, stream, a);
         return;
       }
     }
-    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, JVP>), grid, b32, 0, stream, a);
-    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, JVP>), grid, b32, 0, stream, a);
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, JVP, false, VARIANTS>), grid, b32, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, JVP, false, VARIANTS>), grid, b32, 0, stream, a);
   }
 }
 

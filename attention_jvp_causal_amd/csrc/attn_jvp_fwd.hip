@@ -71,13 +71,15 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   constexpr int NDB = D / 16;  // 16-row blocks of d for the value products
   using Lds = Bf16Lds<D, 4>;
   __shared__ __attribute__((aligned(1024))) Lds s;
+  static_assert(offsetof(Lds, bits) == Lds::bits_off(0), "LDS layout");
+  const uint32_t lds0 = lds_addr(&s);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = wave_uniform(tid >> 6), lane = tid & 63, j16 = lane & 15, g = lane >> 4;
   const int BH = a.B * a.H;
   const TaskCoord tc = task_coord(blockIdx.x, a.n_tasks, BH, a.head_group);
   const int rank = tc.rank, bh = tc.bh;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int qt = a.tasks[rank];
+  const int qt = wave_uniform(a.tasks[rank]);
   const int L = a.L;
   const int64_t in_off = bb * a.isb + hh * a.ish;
   const int64_t kv_off = bb * a.ksb + hh * a.ksh;
@@ -107,17 +109,17 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
   // DMA of key tile kti of entry x (tangent tiles only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
     if (!VARIANTS || x.flags == kTileJvp)
-      issue_tile_loads<kWavesQ16, D, true, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
+      issue_tile_loads<kWavesQ16, D, true, 4>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
-      issue_tile_loads<kWavesQ16, D, false, 4>(s.t[b], plan, src, a.ksl, kti * BN, a.Lk, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(s.bits[b], a.bits, x.pidx, lane);
+      issue_tile_loads<kWavesQ16, D, false, 4>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.bits, x.pidx, lane);
   };
 
-  const int e0 = a.qt_off[qt], e1 = a.qt_off[qt + 1];
+  const int e0 = wave_uniform(a.qt_off[qt]), e1 = wave_uniform(a.qt_off[qt + 1]);
   int e = e0, kt = 0;
   Entry en = {0, 0, -1, 0};
   if (e < e1) {
-    en = a.entries[e];
+    en = load_entry(a.entries + e);
     kt = en.kt0;
     prefetch(0, en, kt);
   }
@@ -310,7 +312,7 @@ void attn_jvp_fwd_bf16_q16_kernel(FwdArgs a) {
     if (kt_n >= en.kt1) {
       e_n = e + 1;
       if (e_n < e1) {
-        en_n = a.entries[e_n];
+        en_n = load_entry(a.entries + e_n);
         kt_n = en_n.kt0;
       }
     }

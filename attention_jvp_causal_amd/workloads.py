@@ -89,6 +89,11 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("wan13b_tf_clean_noisy_h3", 1, 3, 128, "bf16", MASK_TF_CLEAN_NOISY, 21, 1560, 1, seed=7,
                  clean_tangent_zero=True,
                  notes="teacher forcing at 3 heads: one GPU's share of the 12 heads over 4 GPUs"),
+        # Teacher forcing at head_dim 64, for the tangent-free fast path of the
+        # 32-row kernel: the stress workload's head count and frame size.
+        Workload("tf_clean_noisy_d64", 2, 24, 64, "bf16", MASK_TF_CLEAN_NOISY, 21, 880, 3, seed=8,
+                 clean_tangent_zero=True,
+                 notes="teacher forcing c3-3 [21 clean | 21 noisy] frames x 880 tokens, d=64"),
     ]
 }
 

@@ -111,13 +111,15 @@ def test_rect_masks_with_tangent_free_ranges(case):
     compare(w, [to_np(t) for t in got], ref, label="rects")
 
 
-def test_full_size_teacher_forcing_fast_path():
-    w = WORKLOADS["wan13b_tf_clean_noisy"]
+@pytest.mark.parametrize("wname", ["wan13b_tf_clean_noisy", "tf_clean_noisy_d64"])
+def test_full_size_teacher_forcing_fast_path(wname):
+    w = WORKLOADS[wname]
     print(f"[case] full-size {w.name} with the clean half tangent-free", flush=True)
     inputs = make_inputs(w)
     dev = {n: t.cuda() for n, t in inputs.items()}
     base = _layout_desc(w)
     fast = aj.attn_jvp_mask_desc_tangent_free(base, [(0, w.seq_len // 2)])
+    assert fast.work()[1] > 0, "keys-tangent-free tiles present"
     got = _run(dev, fast)
     plain = _run(dev, base)
     _same_as_plain(got, plain, w.name, fast)
