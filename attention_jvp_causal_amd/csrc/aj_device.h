@@ -199,6 +199,8 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  // no load of DMA'd data may be scheduled above the wait
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // max over lanes l and l^32 (the two halves of one q32 query row) without
