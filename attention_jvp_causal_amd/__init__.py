@@ -321,7 +321,12 @@ def _prepare(ins, out_dtype, scale, out, n_out_tensors):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        outs = [torch.empty((B, H, L, D), dtype=odt, device=x0.device) for _ in range(n_out_tensors)]
+        # outputs in the inputs' layout (e.g. [B, L, H, D] storage viewed as
+        # [B, H, L, D]), so that attn_fwd's O can feed attn_bwd, which reads O
+        # with the inputs' strides
+        outs = [torch.empty_like(x0, dtype=odt) for _ in range(n_out_tensors)]
+        if outs[0].stride(3) != 1:
+            outs = [torch.empty((B, H, L, D), dtype=odt, device=x0.device) for _ in range(n_out_tensors)]
         lse = torch.empty((B, H, L), dtype=torch.float32, device=x0.device)
     else:
         *outs, lse = out
@@ -437,7 +442,10 @@ def attn_bwd(q, k, v, o, dout, lse, mask: MaskDesc, scale: Optional[float] = Non
     """dq, dk, dv of masked attention for the cotangent ``dout`` (bf16 inputs).
 
     ``o`` and ``lse`` are the forward's outputs for the same inputs, mask and
-    scale.  Returns (dq, dk, dv, delta): the gradients [B, H, L, D] in
+    scale.  ``o`` and ``dout`` must have q's dtype (bf16) and strides: the C
+    entry point reads all five inputs with one set of strides; attn_fwd's
+    default output has the inputs' layout.  Returns (dq, dk, dv, delta): the
+    gradients [B, H, L, D] in
     ``out_dtype`` (default bf16) and delta = rowsum(dout * o) [B, H, L] float32.
     ``out`` may pass preallocated (dq, dk, dv, delta).
     """

@@ -43,29 +43,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_
 // swz(r) = 4 ((r >> 2) ^ 2 ((r >> 1) & 1)) + 2 (r & 1) meets both.  These lane
 // groupings were inferred from the LDS bank-conflict counter: it reads 0 for
 // this swizzle in the kernels, and about 4 stalled cycles per b128 read for
-// 2 (r % 8) + (r / 8) % 2, which meets only the second condition.
-//
-// At D = 64 a row is 128 bytes and two rows share one 256-byte line of the
-// banks: 16-byte position p of the row in LDS slot s lies in bank unit
-// 8 (s % 2) + p.  Stored in place, the rows k, k+4, k+8, k+12 that one group
-// of a row read serves all have the parity of k, so their 16 chunks meet 8
-// units (a 2-way conflict on every b128 read; the counter read 5.9e8 per
-// launch in the d = 64 dK / dV kernel).  Tile row r is therefore stored in
-// slot slot_q16(r) = r with bits 0 and 2 swapped, which puts two of those rows
-// in each half line, and swz(r) = 2 (r % 4) ^ 4 ((r / 8) % 2) gives the two
-// rows of a half line different bit 2; the eight rows of a transpose read
-// still take four different swz(r) >> 1 in each half line.
+// 2 (r % 8) + (r / 8) % 2, which meets only the second condition.  Built for
+// D = 128 (the JVP and the 16-key dK / dV kernel).  At D = 64, where a row is
+// 128 bytes and two rows share a bank line, the rows k, k+4, k+8, k+12 of one
+// read group always fall in one half line (a 2-way conflict on every b128
+// read); the d = 64 kernels use the 32-row shape and swz_q32 instead.
 template <int D>
 __device__ __forceinline__ int swz_q16(int r) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  return D == 128 ? (((((r >> 2) ^ (((r >> 1) & 1) << 1)) & 3) << 2) | ((r & 1) << 1))
-                  : ((((r & 3) << 1) ^ ((r & 8) >> 1)) & 7);
-}
-// LDS row slot of tile row r (an involution; the identity at D = 128)
-template <int D>
-__device__ __forceinline__ int slot_q16(int r) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  return D == 128 ? r : ((r & ~5) | ((r & 1) << 2) | ((r >> 2) & 1));
+  static_assert(D == 128, "the 16-row tile layout is built for head_dim 128");
+  return ((((r >> 2) ^ (((r >> 1) & 1) << 1)) & 3) << 2) | ((r & 1) << 1);
 }
 template <int D>
 __device__ __forceinline__ int swz_q32(int r) {
@@ -114,22 +100,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Per-lane byte offsets (inside one key tile of one tensor) of the 16-byte
 // chunks this lane moves.  Wave instruction i fills 1 KB block blk = wave +
-// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. slot s = chunk /
-// CH at swizzled position p; the slot holds tile row r = slot(s) (slot is an
-// involution, the identity unless given), so the lane fetches logical chunk
-// p ^ swz(r) of row r.
+// NW*i of the tile: lane l writes LDS chunk blk*64 + l, i.e. row r = chunk /
+// CH at swizzled position p, so it fetches logical chunk p ^ swz(r) of row r.
 template <int NW, int D>
 struct TileLoadPlan {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int NI = (BN * CH) / (64 * NW);   // wave instructions per tensor
   uint32_t voff[NI];
-  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int),
-                                          int (*slot)(int) = nullptr) {
+  __device__ __forceinline__ TileLoadPlan(int64_t sl, int wave, int lane, int (*swz)(int)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int ci = (wave + NW * i) * 64 + lane;
-      const int s = ci / CH, p = ci % CH;
-      const int r = slot ? (s & ~15) | slot(s & 15) : s;
+      const int r = ci / CH, p = ci % CH;
       voff[i] = uint32_t(r * sl * 2 + ((p ^ swz(r)) << 4));
     }
   }

@@ -280,16 +280,16 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
 
 // ---- dK, dV -------------------------------------------------------------------
 
-// Waves of 16 keys per workgroup: 8 (one 128-key tile of the column map, two
-// waves per SIMD) at d = 128; 4 at d = 64, where the kernel fits 168 VGPRs and
-// three 64-key workgroups share a CU, each taking half of a column-map tile.
+// Waves of 16 keys, 8 per workgroup (one 128-key tile of the column map, two
+// waves per SIMD); head_dim 128.  Head_dim 64 runs the 32-key kernel below.
 template <int D>
-constexpr int dkdv_waves() { return D == 64 ? 4 : 8; }
+constexpr int dkdv_waves() { return 8; }
 
 template <int D, bool OUT_F32>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * dkdv_waves<D>(), 64 * dkdv_waves<D>()),
-                          amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
+                          amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(D == 128, "16-key dK / dV waves are built for head_dim 128");
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
   constexpr int NW = dkdv_waves<D>();
@@ -328,7 +328,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vmcnt<0>();
 
-  const TileLoadPlan<NW, D> plan(a.isl, wave, lane, swz_q16<D>, slot_q16<D>);
+  const TileLoadPlan<NW, D> plan(a.isl, wave, lane, swz_q16<D>);
   // Q, dO rows of query tile qti; wave 1 brings their lse and D, wave 0 the
   // key bitmasks of a partial tile
   auto prefetch = [&](int b, const Entry& x, int qti) {
@@ -359,15 +359,15 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   int koff[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = slot_q16<D>(j16) * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = j16 * D + (((4 * ks + g) ^ swz_q16<D>(j16)) << 3);
   const int vrow = 4 * g + (j16 >> 2);
-  // The second read of a pair is 16 rows further on, at the same slot and
-  // swizzle (both depend on the row mod 16): a constant offset of 16 D.
+  // The second read of a pair is 16 rows further on, at the same swizzle
+  // (swz_q16 depends on the row mod 16): a constant offset of 16 D.
   int voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int chunk = 2 * db + ((j16 & 3) >> 1);
-    voff[db] = slot_q16<D>(vrow) * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
+    voff[db] = vrow * D + ((chunk ^ swz_q16<D>(vrow)) << 3) + 4 * (j16 & 1);
   }
 
   int buf = 0;
@@ -381,8 +381,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         qt_n = en_n.kt0;
       }
     }
-    // one barrier per tile (loads landed; other buffer free for the next DMA)
+    // one barrier per tile (loads landed; other buffer free for the next DMA).
+    // Wave 1 brought the tile's 64 lse values, one per lane: it takes them to
+    // log2 units in place before the barrier publishes them, once per query
+    // instead of once per (query, key) element below.
     wait_vmcnt<0>();
+    if (wave == 1) s.rowv[buf][0][lane] *= kLog2e;
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, qt_n);
     const uint16_t* Qt = s.t[buf][0];
@@ -423,8 +427,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
           f32x2_t pv, ds;
-          pv.x = fast_exp2(__builtin_fmaf(S[qb][r], sl2, -lse4[r] * kLog2e));
-          pv.y = fast_exp2(__builtin_fmaf(S[qb][r + 1], sl2, -lse4[r + 1] * kLog2e));
+          pv.x = fast_exp2(__builtin_fmaf(S[qb][r], sl2, -lse4[r]));
+          pv.y = fast_exp2(__builtin_fmaf(S[qb][r + 1], sl2, -lse4[r + 1]));
           if constexpr (MASKED) {
             pv.x = (bits >> (16 * qb + r)) & 1ull ? pv.x : 0.f;
             pv.y = (bits >> (16 * qb + r + 1)) & 1ull ? pv.y : 0.f;
@@ -499,6 +503,227 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ---- dK, dV with 32-key waves (head_dim 64) ------------------------------------
+//
+// The dQ kernel's shape with the roles of queries and keys exchanged: a
+// workgroup of 4 waves owns one 128-key tile of the column map, each wave 32
+// keys, lanes l and l + 32 sharing a key.  K and V of the lane's key are held
+// as MFMA B operands; the 64-query tiles of Q and dO (plus their lse and D)
+// stream through LDS.  With v_mfma_f32_32x32x16_bf16
+//   S = Q K^T,  dP = dO V^T      (rows = queries, columns = keys)
+// put one key per lane column; the accumulator registers are the B operand of
+//   dV^T += dO^T P,  dK^T += Q^T dS
+// with dO^T and Q^T from LDS transpose reads, the same k-slot order as the dQ
+// kernel's K^T.  Against the 16-key waves every Q / dO operand read from LDS
+// serves twice the keys: half the LDS bytes per FLOP, which bound the 16-key
+// kernel at d = 64 (LDS busy 60 %); the register state (about 200 VGPRs) fits
+// two waves per SIMD.  At d = 128 it would need about 300 registers.
+template <int D, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves32, 64 * kDqWaves32), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv32_kernel(BwdArgs a) {
+  static_assert(D == 64, "32-key dK / dV waves are built for head_dim 64");
+  constexpr int NKK = D / 16;  // MFMA k-steps over d for S and dP
+  constexpr int NDB = D / 32;  // 32-row blocks of d for dK^T and dV^T
+  using Lds = BwdLds<D>;
+  __shared__ __attribute__((aligned(1024))) Lds s;
+  static_assert(offsetof(Lds, bits) == Lds::bits_off(0) && offsetof(Lds, rowv) == Lds::rowv_off(0, 0), "LDS layout");
+  const uint32_t lds0 = lds_addr(&s);
+
+  const int tid = threadIdx.x, wave = wave_uniform(tid >> 6), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const TaskCoord tc = task_coord(blockIdx.x, a.n_col_tasks, BH, a.head_group);
+  const int rank = tc.rank, bh = tc.bh;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int ktile = wave_uniform(a.cols.tasks[rank]);
+  const int key_in_tile = wave * 32 + l32;  // row of the tile's bitmask
+  const int L = a.L;
+  const int64_t in_off = bb * a.isb + hh * a.ish;
+  const int64_t bhL = (int64_t)bh * L;
+  const uint16_t* Qg = (const uint16_t*)a.q + in_off;
+  const uint16_t* dOg = (const uint16_t*)a.dout + in_off;
+  const int k_row = ktile * BM + key_in_tile;
+
+  // K, V of this lane's key as B operands (k-step kk: d = 16kk + 8hi ..)
+  bf16x8_t Kr[NKK], Vr[NKK];
+  {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const uint16_t* Kg = (const uint16_t*)a.k + in_off;
+    const uint16_t* Vg = (const uint16_t*)a.v + in_off;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int64_t off = k_row * a.isl + kk * 16 + 8 * hi;
+      Kr[kk] = as_bf16x8(k_row < L ? *(const u32x4_t*)(Kg + off) : zero);
+      Vr[kk] = as_bf16x8(k_row < L ? *(const u32x4_t*)(Vg + off) : zero);
+    }
+  }
+  wait_vmcnt<0>();
+
+  const TileLoadPlan<kDqWaves32, D> plan(a.isl, wave, lane, swz_q32<D>);
+  // Q, dO rows of query tile qti; wave 1 brings their lse and D, wave 0 the
+  // key bitmasks of a partial tile
+  auto prefetch = [&](int b, const Entry& x, int qti) {
+    const int row0 = qti * BN;
+    issue_pair_loads<kDqWaves32, D>(lds0 + Lds::t_off(b), plan, Qg, dOg, a.isl, row0, L, wave);
+    if (wave == 1) {
+      const int nrec = min(L - row0, BN) * 4;
+      lds_dma_4(lds0 + Lds::rowv_off(b, 0), uint32_t(lane) * 4u, make_rsrc(a.lse + bhL + row0, nrec));
+      lds_dma_4(lds0 + Lds::rowv_off(b, 1), uint32_t(lane) * 4u, make_rsrc(a.delta + bhL + row0, nrec));
+    }
+    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.cols.bits, x.pidx, lane);
+  };
+  const int e0 = wave_uniform(a.cols.qt_off[ktile]), e1 = wave_uniform(a.cols.qt_off[ktile + 1]);
+  int e = e0, qtl = 0;
+  Entry en = {0, 0, -1, 0};
+  if (e < e1) {
+    en = load_entry(a.cols.entries + e);
+    qtl = en.kt0;
+    prefetch(0, en, qtl);
+  }
+
+  f32x16_t dKacc[NDB], dVacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dKacc[db][r] = dVacc[db][r] = 0.f;
+  const float sl2 = a.scale_log2;
+
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * D + (((2 * kk + hi) ^ swz_q32<D>(l32)) << 3);
+  const int g = lane >> 4, j = lane & 15;
+  const int vrow0 = 4 * hi + (j >> 2);
+  const int vd0 = 16 * (g & 1) + 4 * (j & 3);
+  int voff[2][NDB];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = vrow0 + 8 * h8;
+      voff[h8][db] = row * D + (((4 * db + (vd0 >> 3)) ^ swz_q32<D>(row)) << 3) + (vd0 & 7);
+    }
+
+  int buf = 0;
+  while (e < e1) {
+    int e_n = e, qt_n = qtl + 1;
+    Entry en_n = en;
+    if (qt_n >= en.kt1) {
+      e_n = e + 1;
+      if (e_n < e1) {
+        en_n = load_entry(a.cols.entries + e_n);
+        qt_n = en_n.kt0;
+      }
+    }
+    // one barrier per tile (loads landed; other buffer free for the next DMA).
+    // Wave 1 brought the tile's 64 lse values, one per lane: it takes them to
+    // log2 units in place before the barrier publishes them, once per query
+    // instead of once per (query, key) element below.
+    wait_vmcnt<0>();
+    if (wave == 1) s.rowv[buf][0][lane] *= kLog2e;
+    __syncthreads();
+    if (e_n < e1) prefetch(buf ^ 1, en_n, qt_n);
+    const bool part = en.pidx >= 0;  // uniform: only partial tiles test the row mask
+    const uint64_t bits = part ? s.bits[buf][key_in_tile] : ~0ull;
+    const uint16_t* Qt = s.t[buf][0];
+    const uint16_t* dOt = s.t[buf][1];
+
+#pragma unroll 1
+    for (int qb = 0; qb < BN / 32; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 queries (lane = key)
+      f32x16_t S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int off = qb * 32 * D + koff[kk];
+        const bf16x8_t qop = as_bf16x8(*(const u32x4_t*)(Qt + off));
+        const bf16x8_t dop = as_bf16x8(*(const u32x4_t*)(dOt + off));
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop, Kr[kk], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dop, Vr[kk], dP, 0, 0, 0);
+      }
+      // lane holds queries qb*32 + 8*(r/4) + 4*hi + r%4 of its key; their
+      // lse and D come from LDS, four consecutive queries per read
+      bf16x8_t P[2], DS[2];
+      auto make_p_ds = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q0 = qb * 32 + 8 * i + 4 * hi;
+          const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][q0]);
+          const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][q0]);
+#pragma unroll
+          for (int t = 0; t < 4; t += 2) {
+            const int r = 4 * i + t;
+            f32x2_t pv, ds;
+            pv.x = fast_exp2(__builtin_fmaf(S[r], sl2, -lse4[t]));
+            pv.y = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -lse4[t + 1]));
+            if constexpr (MASKED) {
+              pv.x = (bits >> (q0 + t)) & 1ull ? pv.x : 0.f;
+              pv.y = (bits >> (q0 + t + 1)) & 1ull ? pv.y : 0.f;
+            }
+            ds.x = pv.x * (dP[r] - del4[t]);
+            ds.y = pv.y * (dP[r + 1] - del4[t + 1]);
+            const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
+            const bf16x2_t d2 = __builtin_convertvector(ds, bf16x2_t);
+            // value step st = i / 2 takes rows 16 st .. 16 st + 15, slots 4 (i % 2) + t
+            const int st = i >> 1, slot = 4 * (i & 1) + t;
+            P[st][slot] = pb.x;
+            P[st][slot + 1] = pb.y;
+            DS[st][slot] = d2.x;
+            DS[st][slot + 1] = d2.y;
+          }
+        }
+      };
+      if (part) make_p_ds(std::true_type{});
+      else make_p_ds(std::false_type{});
+      // dV^T += dO^T P and dK^T += Q^T dS (rows = d, columns = keys)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int off_a = (qb * 32 + 16 * st) * D + voff[0][db];
+          const int off_b = (qb * 32 + 16 * st) * D + voff[1][db];
+          const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_a));
+          const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(dOt + off_b));
+          const s16x4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Qt + off_a));
+          const s16x4_t y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(Qt + off_b));
+          const bf16x8_t oop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8_t qtop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dVacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oop, P[st], dVacc[db], 0, 0, 0);
+          dKacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtop, DS[st], dKacc[db], 0, 0, 0);
+        }
+      }
+    }
+    e = e_n;
+    qtl = qt_n;
+    en = en_n;
+    buf ^= 1;
+  }
+
+  if (k_row < L) {
+    const float c = a.scale;
+    const int64_t out_off = bb * a.osb + hh * a.osh + k_row * a.osl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = db * 32 + 8 * gq + 4 * hi;
+        f32x4_t kv, vv;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          kv[jj] = dKacc[db][4 * gq + jj] * c;
+          vv[jj] = dVacc[db][4 * gq + jj];
+        }
+        if constexpr (OUT_F32) {
+          *(f32x4_t*)((float*)a.dk + out_off + d0) = kv;
+          *(f32x4_t*)((float*)a.dv + out_off + d0) = vv;
+        } else {
+          *(bf16x4_t*)((__bf16*)a.dk + out_off + d0) = __builtin_convertvector(kv, bf16x4_t);
+          *(bf16x4_t*)((__bf16*)a.dv + out_off + d0) = __builtin_convertvector(vv, bf16x4_t);
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 template <int D, bool OUT_F32>
@@ -506,13 +731,20 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   constexpr int NW = dkdv_waves<D>();
   hipLaunchKernelGGL((attn_bwd_dq32_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_row_tasks) * a.B * a.H)),
                      dim3(64 * kDqWaves32), 0, stream, a);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>),
-                     dim3(unsigned(int64_t(a.n_col_tasks) * (BM / (16 * NW)) * a.B * a.H)), dim3(64 * NW), 0, stream,
-                     a);
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((attn_bwd_dkdv32_kernel<D, OUT_F32>), dim3(unsigned(int64_t(a.n_col_tasks) * a.B * a.H)),
+                       dim3(64 * kDqWaves32), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, OUT_F32>),
+                       dim3(unsigned(int64_t(a.n_col_tasks) * (BM / (16 * NW)) * a.B * a.H)), dim3(64 * NW), 0,
+                       stream, a);
+  }
 }
 
 int launch_bwd(BwdArgs a, int out_dtype, int head_dim, hipStream_t stream) {
-  const int64_t parts = head_dim == 64 ? BM / (16 * dkdv_waves<64>()) : BM / (16 * dkdv_waves<128>());
+  // key-parallel workgroups per column-map tile: one 4 x 32-key workgroup at
+  // d = 64, one 8 x 16-key workgroup at 128
+  const int64_t parts = head_dim == 64 ? 1 : BM / (16 * dkdv_waves<128>());
   const int64_t g1 = int64_t(a.n_row_tasks) * a.B * a.H, g2 = int64_t(a.n_col_tasks) * parts * a.B * a.H;
   if (g1 <= 0 || g2 <= 0 || g1 > 0x7fffffff || g2 > 0x7fffffff) return AJ_EINVAL;
   a.head_group = head_group_for(a.B * a.H);

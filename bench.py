@@ -46,40 +46,18 @@ METRIC = "masked attention-JVP TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak,
 METRIC_FWD = "masked attention forward TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_BWD = "masked attention backward TFLOP/s (unmasked FLOPs, 10d per pair) and % of bf16 MFMA peak, 1 GPU"
 METRIC_KV = "KV-cache chunk attention TFLOP/s (unmasked FLOPs, 4d per pair) and % of bf16 MFMA peak, 1 GPU"
-# What each JVP kernel is built from: its source file and the headers it
-# includes (the 16-row kernel at head_dim 128, the 32-row kernel at 64).
-_CSRC = os.path.join(ROOT, "attention_jvp_causal_amd", "csrc")
-KERNEL_SRCS = {
-    "attn_jvp_fwd.hip": [os.path.join(_CSRC, n) for n in ("aj_tiles.h", "aj_launch.h", "aj_device.h",
-                                                          "attn_jvp_fwd.hip")],
-    "attn_fwd_q32.hip": [os.path.join(ROOT, "include", "attn_jvp.h")] +
-                        [os.path.join(_CSRC, n) for n in ("aj_tiles.h", "aj_launch.h", "aj_device.h",
-                                                          "attn_fwd_q32.hip")],
-}
-
-
-def kernel_source(head_dim: int) -> str:
-    return "attn_jvp_fwd.hip" if head_dim == 128 else "attn_fwd_q32.hip"
-
-
-def kernel_sha(source: str = "attn_jvp_fwd.hip") -> str:
-    """Hash of a JVP kernel's sources with comments and blank lines removed,
-    and of the compiler flags they are built with (include paths aside), so
-    that a counter record stays valid across comment-only edits and no
-    longer."""
-    import re
-
+def kernel_isa_sha(kernel: str):
+    """Hash of a kernel instance's generated code, as the build recorded it
+    (attention_jvp_causal_amd/libattnjvp.isa.json); kernel is the name
+    kernel_name() returns.  None when the build wrote no entry for it."""
     from attention_jvp_causal_amd import build as _build
 
-    src = ""
-    for path in KERNEL_SRCS[source]:
-        with open(path) as f:
-            src += f.read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", "", src)
-    code = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
-    flags = " ".join(f for f in _build.compile_flags(source) if not f.startswith("-I"))
-    return hashlib.sha256((code + "\n" + flags).encode()).hexdigest()[:16]
+    if not os.path.exists(_build.ISA_PATH):
+        return None
+    with open(_build.ISA_PATH) as f:
+        isa = json.load(f)
+    key = f"void aj::{kernel}(aj::FwdArgs)"
+    return isa.get(key)
 
 
 def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tangent_free: bool = False,
@@ -88,10 +66,11 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
     b = lambda x: "true" if x else "false"
     o = b(out_f32)
     if op == "bwd":
-        return f"attn_bwd_dq32_kernel<{head_dim}, {o}> + attn_bwd_dkdv_kernel<{head_dim}, {o}>"
+        dkdv = f"attn_bwd_dkdv32_kernel<64, {o}>" if head_dim == 64 else f"attn_bwd_dkdv_kernel<{head_dim}, {o}>"
+        return f"attn_bwd_dq32_kernel<{head_dim}, {o}> + {dkdv}"
     if dtype == "f32":
         return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
-    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false>"
+    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false, false>"
     if op in ("fwd", "kv"):
         return primal
     if head_dim == 128:
@@ -99,7 +78,7 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
     else:
         s = 1.0 / math.sqrt(head_dim) if scale is None else scale
         m, _ = math.frexp(s)
-        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}>"
+        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}, {b(tangent_free)}>"
     # a tangent-free descriptor runs its primal-only query tiles through the
     # primal kernel first
     return f"{primal} + {jvp}" if tangent_free else jvp
@@ -107,15 +86,15 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from the rocprofv3 counter runs recorded under
-    profiles/, or None if they were taken on a different kernel source."""
-    from attention_jvp_causal_amd.workloads import WORKLOADS
-
+    profiles/, or None if they were taken on other code than the kernel the
+    current build holds."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path) or workload not in WORKLOADS:
+    if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_sha(kernel_source(WORKLOADS[workload].head_dim)):
+    isa = kernel_isa_sha(rec.get("kernel", ""))
+    if isa is None or rec.get("kernel_isa") != isa:
         return None
     return rec.get("bytes_per_launch")
 
@@ -157,7 +136,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int
     rec = {
         "workload": workload,
         "kernel": kname,
-        "kernel_sha": kernel_sha(kernel_source(w.head_dim)),
+        "kernel_isa": kernel_isa_sha(kname),
         "fetch_size_kib_per_dispatch": round(fk, 1),
         "write_size_kib_per_dispatch": round(wk, 1),
         "dispatches_averaged": [nf, nw],

@@ -20,14 +20,31 @@ def test_more_than_one_gpu_is_refused():
 
 def test_kernel_names_follow_the_dispatch():
     assert bench.kernel_name("bf16", 128, False) == "attn_jvp_fwd_bf16_q16_kernel<128, false, false>"
-    assert bench.kernel_name("bf16", 64, False, scale=0.125) == "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true>"
-    assert bench.kernel_name("bf16", 64, False, scale=0.1) == "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false>"
-    assert bench.kernel_name("bf16", 128, True, op="fwd") == "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false>"
+    assert bench.kernel_name("bf16", 64, False, scale=0.125) == \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false>"
+    assert bench.kernel_name("bf16", 64, False, scale=0.1) == \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, false>"
+    assert bench.kernel_name("bf16", 128, True, op="fwd") == \
+        "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false>"
     assert bench.kernel_name("bf16", 128, False, op="bwd") == \
         "attn_bwd_dq32_kernel<128, false> + attn_bwd_dkdv_kernel<128, false>"
+    assert bench.kernel_name("bf16", 64, False, op="bwd") == \
+        "attn_bwd_dq32_kernel<64, false> + attn_bwd_dkdv32_kernel<64, false>"
     assert bench.kernel_name("bf16", 128, False, tangent_free=True) == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false> + attn_jvp_fwd_bf16_q16_kernel<128, false, true>"
+        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false> + attn_jvp_fwd_bf16_q16_kernel<128, false, true>"
+    assert bench.kernel_name("bf16", 64, False, tangent_free=True) == \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false> + " \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true>"
     assert bench.kernel_name("f32", 64, True) == "attn_jvp_fwd_f32_kernel<64>"
+
+
+def test_every_launched_kernel_has_a_code_hash():
+    # the build records a hash of each kernel's generated code; every JVP
+    # instance bench.py can name must be among them
+    for D, scale in ((128, None), (64, 0.125), (64, 0.1)):
+        for tf in (False, True):
+            for name in bench.kernel_name("bf16", D, False, tangent_free=tf, scale=scale).split(" + "):
+                assert bench.kernel_isa_sha(name), name
 
 
 def test_clock_sampler_reads_the_starred_level(tmp_path):
@@ -67,6 +84,6 @@ def test_traffic_records_match_the_kernel_sources():
         with open(path) as f:
             rec = json.load(f)
         w = WORKLOADS[rec["workload"]]
-        assert rec["kernel_sha"] == bench.kernel_sha(bench.kernel_source(w.head_dim)), path
         assert rec["kernel"] == bench.kernel_name(w.dtype, w.head_dim, False, scale=w.scale), path
+        assert rec["kernel_isa"] == bench.kernel_isa_sha(rec["kernel"]), path
         assert bench.measured_traffic(w.name) == rec["bytes_per_launch"] > 0, path

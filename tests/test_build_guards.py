@@ -58,7 +58,7 @@ OCCUPANCY = [
     (r"attn_bwd_dq32_kernelILi128E", 2),
     (r"attn_bwd_dq32_kernelILi64E", 3),
     (r"attn_bwd_dkdv_kernelILi128E", 2),
-    (r"attn_bwd_dkdv_kernelILi64E", 3),
+    (r"attn_bwd_dkdv32_kernelILi64E", 2),
 ]
 
 
