@@ -70,10 +70,11 @@ def test_clock_sampler_without_sysfs_reports_nothing():
     assert c.stop() is None
 
 
-def test_traffic_records_match_the_kernel_sources():
+def test_traffic_records_match_the_kernel_code():
     # bench.py reports roofline.traffic only while the counter record was
-    # taken on the current kernel sources and flags; a kernel change needs a
-    # new record (bench.py --record-traffic).  The bench workload must have one.
+    # taken on the kernel code the build produced (the hash of its gfx950
+    # instructions); a change to that code needs a new record
+    # (bench.py --record-traffic).  The bench workload must have one.
     import glob
 
     from attention_jvp_causal_amd.workloads import BENCH_WORKLOAD, WORKLOADS
