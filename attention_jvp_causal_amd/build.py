@@ -66,7 +66,9 @@ def compile_flags(src: str | None = None):
 def kernel_isa_hashes(asm: str) -> dict:
     """{demangled kernel name: sha256[:16] of its instructions} for the kernels
     in one device assembly listing (comments, blank lines and assembler
-    directives left out)."""
+    directives left out; branch labels without the function number the
+    assembler gives them, which moves when other kernels are added to the
+    file)."""
     bodies = {}
     kernels = set(re.findall(r"^\s*\.amdhsa_kernel (\S+)", asm, flags=re.M))
     for m in re.finditer(r"^(\S+):(?:\s*;.*)?$", asm, flags=re.M):
@@ -78,7 +80,7 @@ def kernel_isa_hashes(asm: str) -> dict:
         for line in asm[m.end():end].splitlines():
             line = line.split(";")[0].split("//")[0].strip()
             if line and not line.startswith("."):
-                lines.append(line)
+                lines.append(re.sub(r"\.LBB\d+_", ".LBB_", line))
         bodies[name] = hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
     if not bodies:
         return {}

@@ -174,6 +174,13 @@ __device__ __forceinline__ void issue_pair_loads(uint32_t lds_buf, const TileLoa
 __device__ __forceinline__ void issue_bits_load(uint32_t lds_bits, const uint64_t* bits, int pidx, int lane) {
   lds_dma_16(lds_bits, uint32_t(lane) * 16u, make_rsrc(bits + (int64_t)pidx * BM, BM * 8));
 }
+// The same for a partial tile of a 256-row task: wave w < 2 loads rows
+// 128 w .. 128 w + 127 (1 KB) to LDS byte address lds_bits + 1024 w.
+__device__ __forceinline__ void issue_bits_load_wide(uint32_t lds_bits, const uint64_t* bits, int pidx, int wave,
+                                                     int lane) {
+  lds_dma_16(lds_bits + wave * 1024, uint32_t(lane) * 16u,
+             make_rsrc(bits + (int64_t)pidx * kTileMWide + wave * BM, BM * 8));
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
@@ -239,16 +246,16 @@ __device__ __forceinline__ void bf16_chunks_to_f16(uint16_t* t0, uint16_t* t1, i
 // Key-tile buffers of the bf16 kernels: NT = 4 tensors (K, tK, V, tV) for the
 // JVP, NT = 2 (K, V) for the primal forward, whose smaller footprint lets two
 // workgroups share a CU.
-template <int D, int NT>
+template <int D, int NT, int ROWS = BM>
 struct Bf16Lds {
   static constexpr int TILE = BN * D;  // elements per tensor tile
   uint16_t t[2][NT][TILE];             // [buffer][tensor]
-  uint64_t bits[2][BM];                // per-row key bitmask of a partial tile
+  uint64_t bits[2][ROWS];              // per-row key bitmask of a partial tile (ROWS query rows)
   // LDS slot of tensor t in {0: K, 1: tK, 2: V, 3: tV}
   static constexpr __device__ int slot(int t) { return NT == 4 ? t : t / 2; }
   // byte offsets of t[b][0] and bits[b] from the start of the struct
   static constexpr __device__ uint32_t t_off(int b) { return uint32_t(b) * NT * TILE * 2; }
-  static constexpr __device__ uint32_t bits_off(int b) { return 2u * NT * TILE * 2 + uint32_t(b) * BM * 8; }
+  static constexpr __device__ uint32_t bits_off(int b) { return 2u * NT * TILE * 2 + uint32_t(b) * ROWS * 8; }
 };
 // Issues the DMA of key tile [key0, key0 + BN) of K and V, and of tK and tV
 // when TANG, into one LDS buffer.  Returns immediately; completion is tracked

@@ -19,13 +19,14 @@ constexpr int kMaxDevices = 64;
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 inline bool supported_dtype(int t) { return t == AJ_F32 || t == AJ_BF16; }
 
-// A tile map over one orientation of the mask: for every tile of kTileM
-// rows (the "owner" axis) the runs of kTileN-wide tiles of the other axis it
+// A tile map over one orientation of the mask: for every tile of bm (kTileM
+// or kTileMWide) rows of the "owner" axis the runs of kTileN-wide tiles of the other axis it
 // must visit, per-row bitmasks of its partial tiles and a longest-first task
 // order.  The row map (owner = query tiles) drives the forward kernels and the
 // dQ kernel; the column map (owner = key tiles, built from the transposed
 // rectangles) drives the dK / dV kernel.
 struct TileMap {
+  int32_t bm = kTileM;              // rows (owner-axis tokens) per owner tile
   int32_t n_qt = 0, n_kt = 0;       // owner tiles, visited-axis tiles
   int32_t full_tiles = 0, partial_tiles = 0;
   int64_t pairs_by_var[3] = {0, 0, 0};  // allowed pairs in kTileJvp / KeysFree / AllFree tiles
@@ -37,12 +38,12 @@ struct TileMap {
   // of the JVP but the primal remains), n_primal_tasks of them, then the rest.
   std::vector<int32_t> tasks_split;
   int32_t n_primal_tasks = 0;
-  std::vector<uint64_t> bits;       // partial_tiles * kTileM words
+  std::vector<uint64_t> bits;       // partial_tiles * bm words
 };
 
 struct DeviceTables {
-  void* base = nullptr;  // one hipMalloc holding both maps
-  DeviceMap rows, cols;
+  void* base = nullptr;  // one hipMalloc holding the three maps
+  DeviceMap rows, cols, rows_w;
   // set once base and the maps are valid (attn_jvp_mask_desc_upload); launches
   // read the tables without taking the descriptor's lock
   std::atomic<bool> ready{false};
@@ -59,6 +60,7 @@ struct aj_mask_desc {
   std::vector<int32_t> tfree;       // merged tangent-free token ranges {t0,t1}
   aj::TileMap rows;                 // query tiles -> key-tile runs
   aj::TileMap cols;                 // key tiles -> query-tile runs (transposed mask)
+  aj::TileMap rows_w;               // query tiles of kTileMWide rows -> key-tile runs (no variants)
   std::mutex mu;                    // serialises uploads into dev[]
   aj::DeviceTables dev[aj::kMaxDevices];
 };

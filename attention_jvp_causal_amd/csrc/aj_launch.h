@@ -31,6 +31,7 @@ struct FwdArgs {
   const Entry* entries;
   const int32_t* tasks;
   const uint64_t* bits;
+  int32_t tile_m;  // query rows per task: kTileM, or kTileMWide (the primal forward's wide map)
 };
 
 // Arguments of the gradient kernels (bf16 inputs [B, H, L, D] sharing the

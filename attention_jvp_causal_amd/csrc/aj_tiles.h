@@ -11,6 +11,11 @@ namespace aj {
 // bitmask row is one 64-bit word.
 constexpr int kTileM = 128;
 constexpr int kTileN = 64;
+// Query rows per workgroup of the primal forward at head_dim 128: eight
+// 32-row waves (two per SIMD, one workgroup per CU) share one key stream, half
+// the key-tile traffic per FLOP of two 128-row workgroups.  It has a tile map
+// of its own (aj_mask_desc::rows_w).
+constexpr int kTileMWide = 256;
 
 // Which tangents a (query tile, key tile) pair carries, from the caller's
 // declaration of tokens whose tangents are zero (Entry::flags):

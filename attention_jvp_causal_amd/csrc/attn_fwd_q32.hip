@@ -58,19 +58,27 @@ __device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
 template <int D, bool JVP>
 constexpr int q32_waves_per_simd() { return D == 64 && !JVP ? 3 : 2; }
 
+// NWV: waves per workgroup, 4 (128-row tasks of the descriptor's row map) or,
+// for the primal forward at d = 128, 8 (256-row tasks of its wide map): the
+// eight waves fill the CU's two waves per SIMD as one workgroup, so every
+// streamed key tile serves 256 rows, half the DMA and LDS writes per FLOP of
+// two 128-row workgroups (5 % on the KV-cache step).
+//
 // VARIANTS (JVP only): the descriptor declares tangent-free tokens; tiles whose
 // keys carry no tangent skip the tK and tV DMA, reads and products, the others
 // run them.  Tiles where neither queries nor keys carry tangents take the same
 // keys-tangent-free path: their tQ is zero, so their score tangents and u are
 // exact zeros.
-template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false, bool VARIANTS = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWavesQ32, 64 * kWavesQ32),
+template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false, bool VARIANTS = false, int NWV = kWavesQ32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV),
                           amdgpu_waves_per_eu(q32_waves_per_simd<D, JVP>(), q32_waves_per_simd<D, JVP>())))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
+  static_assert(NWV == kWavesQ32 || (NWV == 8 && D == 128 && !JVP), "8-wave workgroups: d = 128 primal only");
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
   constexpr int NT = JVP ? 4 : 2;
-  using Lds = Bf16Lds<D, NT>;
+  constexpr int BMW = 32 * NWV;  // query rows per task
+  using Lds = Bf16Lds<D, NT, BMW>;
   // The JVP runs its value products in fp16: V and tV are converted in LDS
   // (exact for bf16 values of magnitude in [2^-14, 65504]), and p~ 2^-8 and
   // u = p~ 2^-8 (c ts) are rounded to fp16 (11 significant bits against
@@ -99,16 +107,20 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
   const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
                                   (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
-  const int q_row = qt * BM + wave * 32 + l32;
+  const int q_row = qt * BMW + wave * 32 + l32;
 
-  const TileLoadPlan<kWavesQ32, D> plan(a.ksl, wave, lane, swz_q32<D>);
+  const TileLoadPlan<NWV, D> plan(a.ksl, wave, lane, swz_q32<D>);
   // DMA of key tile kti of entry x (tK and tV only where x carries them)
   auto prefetch = [&](int b, const Entry& x, int kti) {
     if (JVP && (!VARIANTS || x.flags == kTileJvp))
-      issue_tile_loads<kWavesQ32, D, true, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
+      issue_tile_loads<NWV, D, true, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
     else
-      issue_tile_loads<kWavesQ32, D, false, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
-    if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.bits, x.pidx, lane);
+      issue_tile_loads<NWV, D, false, NT>(lds0 + Lds::t_off(b), plan, src, a.ksl, kti * BN, a.Lk, wave);
+    if constexpr (NWV == 8) {
+      if (x.pidx >= 0 && wave < 2) issue_bits_load_wide(lds0 + Lds::bits_off(b), a.bits, x.pidx, wave, lane);
+    } else {
+      if (x.pidx >= 0 && wave == 0) issue_bits_load(lds0 + Lds::bits_off(b), a.bits, x.pidx, lane);
+    }
   };
 
   // first key tile in flight before the prologue
@@ -341,9 +353,9 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     // before the barrier publishes them
     if constexpr (F16) {
       if (!VARIANTS || en.flags == kTileJvp)
-        bf16_chunks_to_f16<kWavesQ32, D, 2>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
+        bf16_chunks_to_f16<NWV, D, 2>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
       else
-        bf16_chunks_to_f16<kWavesQ32, D, 1>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
+        bf16_chunks_to_f16<NWV, D, 1>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
     }
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, kt_n);
@@ -582,8 +594,14 @@ void attn_jvp_fwd_f32_kernel(FwdArgs a) {
 template <bool JVP, bool VARIANTS>
 static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid, hipStream_t stream) {
   const dim3 b32(64 * kWavesQ32);
-  if (!JVP && head_dim == 128) {
-    // primal forward: 32-row waves, two workgroups per CU
+  if (!JVP && head_dim == 128 && a.tile_m == kTileMWide) {
+    // primal forward on the wide map: 8 x 32-row waves, one workgroup per CU
+    const dim3 b256(64 * 8);
+    if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false, 8>), grid, b256, 0, stream, a);
+    else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 8>), grid, b256, 0, stream, a);
+  } else if (!JVP && head_dim == 128) {
+    // primal forward on the row map (the primal-only query tiles of a
+    // tangent-free JVP): 4 x 32-row waves, two workgroups per CU
     if (out_f32) hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, true, false>), grid, b32, 0, stream, a);
     else hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<128, false, false>), grid, b32, 0, stream, a);
   } else if (head_dim == 128) {

@@ -50,7 +50,7 @@ int32_t upload_tables(aj_mask_desc* d, int dev) {
   DeviceTables& t = d->dev[dev];
   if (t.ready.load(std::memory_order_acquire)) return AJ_OK;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-  // layout: [rows map | cols map], each {qt_off | entries | tasks | tasks_split | bits}
+  // layout: [rows map | cols map | wide rows map], each {qt_off | entries | tasks | tasks_split | bits}
   struct Part {
     const void* src;
     size_t bytes, off;
@@ -61,7 +61,7 @@ int32_t upload_tables(aj_mask_desc* d, int dev) {
     parts.push_back(Part{src, bytes, total});
     total += align(std::max<size_t>(bytes, 16));
   };
-  for (const aj::TileMap* m : {&d->rows, &d->cols}) {
+  for (const aj::TileMap* m : {&d->rows, &d->cols, &d->rows_w}) {
     add(m->qt_off.data(), m->qt_off.size() * sizeof(int32_t));
     add(m->entries.data(), m->entries.size() * sizeof(Entry));
     add(m->tasks.data(), m->tasks.size() * sizeof(int32_t));
@@ -78,8 +78,8 @@ int32_t upload_tables(aj_mask_desc* d, int dev) {
     return AJ_EHIP;
   }
   uint8_t* b = static_cast<uint8_t*>(base);
-  aj::DeviceMap* dm[2] = {&t.rows, &t.cols};
-  for (int i = 0; i < 2; ++i) {
+  aj::DeviceMap* dm[3] = {&t.rows, &t.cols, &t.rows_w};
+  for (int i = 0; i < 3; ++i) {
     dm[i]->qt_off = reinterpret_cast<const int32_t*>(b + parts[5 * i].off);
     dm[i]->entries = reinterpret_cast<const Entry*>(b + parts[5 * i + 1].off);
     dm[i]->tasks = reinterpret_cast<const int32_t*>(b + parts[5 * i + 2].off);
@@ -167,6 +167,7 @@ int32_t prepare_geom(const Geometry& s, const void* const* ins, int n_in, const 
   r.osb = s.os[0]; r.osh = s.os[1]; r.osl = s.os[2];
   r.B = s.B; r.H = s.H; r.L = s.Lq; r.Lk = s.Lk;
   r.n_tasks = mask->rows.n_qt;
+  r.tile_m = aj::kTileM;
   r.scale = scale;
   r.scale_log2 = float(double(scale) * 1.4426950408889634074);
   r.qt_off = t->rows.qt_off; r.entries = t->rows.entries; r.tasks = t->rows.tasks; r.bits = t->rows.bits;
@@ -177,6 +178,19 @@ int32_t prepare(const aj_shape* s, const void* const* ins, int n_in, const void*
                 const aj_mask_desc* mask, float scale, aj::FwdArgs* a) {
   if (!s) return AJ_EINVAL;
   return prepare_geom(from_shape(s), ins, n_in, outs, n_out, mask, scale, a);
+}
+
+// The primal forward at head_dim 128 runs 256-row tasks: point the launch at
+// the descriptor's wide map (after prepare_geom has checked the tables).
+int32_t use_wide_map(const aj_mask_desc* mask, int32_t head_dim, aj::FwdArgs* a) {
+  if (head_dim != 128) return AJ_OK;
+  const DeviceTables* t = nullptr;
+  int32_t st = device_tables(mask, &t);
+  if (st != AJ_OK) return st;
+  a->n_tasks = mask->rows_w.n_qt;
+  a->tile_m = aj::kTileMWide;
+  a->qt_off = t->rows_w.qt_off; a->entries = t->rows_w.entries; a->tasks = t->rows_w.tasks; a->bits = t->rows_w.bits;
+  return AJ_OK;
 }
 
 }  // namespace
@@ -384,6 +398,7 @@ int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v,
   const void* outs[2] = {o, lse};
   aj::FwdArgs a;
   int32_t st = prepare(s, ins, 3, outs, 2, mask, scale, &a);
+  if (st == AJ_OK) st = use_wide_map(mask, s->head_dim, &a);
   if (st != AJ_OK) return st;
   a.tq = a.tk = a.tv = nullptr;
   a.to = nullptr;
@@ -457,6 +472,7 @@ int32_t attn_fwd_kv(const aj_kv_shape* s, const void* q, const void* k, const vo
   const void* outs[2] = {o, lse};
   aj::FwdArgs a;
   int32_t st = prepare_geom(g, ins, 3, outs, 2, mask, scale, &a);
+  if (st == AJ_OK) st = use_wide_map(mask, s->head_dim, &a);
   if (st != AJ_OK) return st;
   a.tq = a.tk = a.tv = nullptr;
   a.to = nullptr;

@@ -119,12 +119,13 @@ int32_t layout_rects(const aj_mask_spec* s, int32_t L, std::vector<int32_t>* out
 }
 
 // Tile map of rectangles r (owner axis first: {o0, o1, v0, v1}) with owner
-// tiles of kTileM over [0, Lo) and visited tiles of kTileN over [0, Lv).
+// tiles of BM rows over [0, Lo) and visited tiles of kTileN over [0, Lv).
 // tfree (merged ranges) marks tangent-free tokens (square masks: both axes
 // index the same sequence).
 static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const std::vector<int32_t>& tfree,
-                      TileMap* m) {
-  const int32_t BM = kTileM, BN = kTileN;
+                      int32_t BM, TileMap* m) {
+  const int32_t BN = kTileN;
+  m->bm = BM;
   m->n_qt = (Lo + BM - 1) / BM;
   m->n_kt = (Lv + BN - 1) / BN;
   // tangent-free owner and visited tiles: every token of the tile inside
@@ -270,7 +271,9 @@ int32_t build_from_rects(int32_t Lq, int32_t Lk, const int32_t* r, int32_t n, in
     d->rects.assign(r, r + 4 * size_t(n));
     d->tfree = tfree;
     for (int32_t i = 0; i < n; ++i) d->pairs += int64_t(r[4 * i + 1] - r[4 * i]) * (r[4 * i + 3] - r[4 * i + 2]);
-    build_map(Lq, Lk, r, n, tfree, &d->rows);
+    build_map(Lq, Lk, r, n, tfree, kTileM, &d->rows);
+    // the primal forward's wide query tiles (no tangents, so no variants)
+    build_map(Lq, Lk, r, n, std::vector<int32_t>(), kTileMWide, &d->rows_w);
     // the transposed mask: key tiles own runs of query tiles (no variants)
     std::vector<int32_t> tr(4 * size_t(n));
     for (int32_t i = 0; i < n; ++i) {
@@ -279,7 +282,7 @@ int32_t build_from_rects(int32_t Lq, int32_t Lk, const int32_t* r, int32_t n, in
       tr[4 * i + 2] = r[4 * i];
       tr[4 * i + 3] = r[4 * i + 1];
     }
-    build_map(Lk, Lq, tr.data(), n, std::vector<int32_t>(), &d->cols);
+    build_map(Lk, Lq, tr.data(), n, std::vector<int32_t>(), kTileM, &d->cols);
   } catch (const std::bad_alloc&) {
     delete d;
     return AJ_ENOMEM;

@@ -70,15 +70,18 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
         return f"attn_bwd_dq32_kernel<{head_dim}, {o}> + {dkdv}"
     if dtype == "f32":
         return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
-    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false, false>"
+    # the last template argument is the workgroup's wave count: the primal
+    # forward at d = 128 runs 8-wave (256-row) tasks, the primal-only tiles of
+    # a tangent-free JVP and every other q32 instance 4-wave (128-row) ones
+    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false, false, 4>"
     if op in ("fwd", "kv"):
-        return primal
+        return primal if head_dim == 64 else f"attn_jvp_fwd_bf16_q32_kernel<128, {o}, false, false, false, 8>"
     if head_dim == 128:
         jvp = f"attn_jvp_fwd_bf16_q16_kernel<128, {o}, {b(tangent_free)}>"
     else:
         s = 1.0 / math.sqrt(head_dim) if scale is None else scale
         m, _ = math.frexp(s)
-        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}, {b(tangent_free)}>"
+        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}, {b(tangent_free)}, 4>"
     # a tangent-free descriptor runs its primal-only query tiles through the
     # primal kernel first
     return f"{primal} + {jvp}" if tangent_free else jvp

@@ -21,30 +21,39 @@ def test_more_than_one_gpu_is_refused():
 def test_kernel_names_follow_the_dispatch():
     assert bench.kernel_name("bf16", 128, False) == "attn_jvp_fwd_bf16_q16_kernel<128, false, false>"
     assert bench.kernel_name("bf16", 64, False, scale=0.125) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false, 4>"
     assert bench.kernel_name("bf16", 64, False, scale=0.1) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, false>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, false, 4>"
+    # the primal forward (and the KV step) at d = 128 runs 8-wave, 256-row tasks
     assert bench.kernel_name("bf16", 128, True, op="fwd") == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false>"
+        "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false, 8>"
+    assert bench.kernel_name("bf16", 128, False, op="kv") == \
+        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 8>"
+    assert bench.kernel_name("bf16", 64, False, op="fwd") == \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4>"
     assert bench.kernel_name("bf16", 128, False, op="bwd") == \
         "attn_bwd_dq32_kernel<128, false> + attn_bwd_dkdv_kernel<128, false>"
     assert bench.kernel_name("bf16", 64, False, op="bwd") == \
         "attn_bwd_dq32_kernel<64, false> + attn_bwd_dkdv32_kernel<64, false>"
+    # the primal-only query tiles of a tangent-free JVP keep 4-wave tasks
     assert bench.kernel_name("bf16", 128, False, tangent_free=True) == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false> + attn_jvp_fwd_bf16_q16_kernel<128, false, true>"
+        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 4> + " \
+        "attn_jvp_fwd_bf16_q16_kernel<128, false, true>"
     assert bench.kernel_name("bf16", 64, False, tangent_free=True) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false> + " \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4> + " \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true, 4>"
     assert bench.kernel_name("f32", 64, True) == "attn_jvp_fwd_f32_kernel<64>"
 
 
 def test_every_launched_kernel_has_a_code_hash():
-    # the build records a hash of each kernel's generated code; every JVP
+    # the build records a hash of each kernel's generated code; every forward
     # instance bench.py can name must be among them
     for D, scale in ((128, None), (64, 0.125), (64, 0.1)):
         for tf in (False, True):
             for name in bench.kernel_name("bf16", D, False, tangent_free=tf, scale=scale).split(" + "):
                 assert bench.kernel_isa_sha(name), name
+        for op in ("fwd", "kv"):
+            assert bench.kernel_isa_sha(bench.kernel_name("bf16", D, False, op=op)), (D, op)
 
 
 def test_clock_sampler_reads_the_starred_level(tmp_path):
