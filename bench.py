@@ -56,8 +56,7 @@ def kernel_isa_sha(kernel: str):
         return None
     with open(_build.ISA_PATH) as f:
         isa = json.load(f)
-    key = f"void aj::{kernel}(aj::FwdArgs)"
-    return isa.get(key)
+    return isa.get(f"void aj::{kernel}(aj::FwdArgs)") or isa.get(f"void aj::{kernel}(aj::BwdArgs)")
 
 
 def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tangent_free: bool = False,

@@ -54,6 +54,8 @@ def test_every_launched_kernel_has_a_code_hash():
                 assert bench.kernel_isa_sha(name), name
         for op in ("fwd", "kv"):
             assert bench.kernel_isa_sha(bench.kernel_name("bf16", D, False, op=op)), (D, op)
+        for name in bench.kernel_name("bf16", D, False, op="bwd").split(" + "):
+            assert bench.kernel_isa_sha(name), name
 
 
 def test_clock_sampler_reads_the_starred_level(tmp_path):
