@@ -143,6 +143,11 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
   const float lse_l2 = q_row < L ? a.lse[bhL + q_row] * kLog2e : 0.f;
   wait_vmcnt<0>();
   const float delta = dpart + wave_xor32(dpart);
+  // dP^T chains start from -D (the lane's row value in all 16 registers), so
+  // they deliver dP - D and dS = P (dP - D) takes one multiply per element
+  f32x16_t negD;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD[r] = -delta;
 
   const TileLoadPlan<kDqWaves32, D> plan(a.isl, wave, lane, swz_q32<D>);
   auto prefetch = [&](int b, const Entry& x, int kti) {
@@ -203,9 +208,9 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
 #pragma unroll 1
     for (int kb = 0; kb < BN / 32; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T for 32 keys (lane = query)
-      f32x16_t S, dP;
+      f32x16_t S, dP = negD;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
+      for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = kb * 32 * D + koff[kk];
@@ -226,8 +231,8 @@ void attn_bwd_dq32_kernel(BwdArgs a) {
             const float p0 = fast_exp2(__builtin_fmaf(S[r], sl2, -lse_l2));
             const float p1 = fast_exp2(__builtin_fmaf(S[r + 1], sl2, -lse_l2));
             f32x2_t ds;
-            ds.x = p0 * (dP[r] - delta);
-            ds.y = p1 * (dP[r + 1] - delta);
+            ds.x = p0 * dP[r];
+            ds.y = p1 * dP[r + 1];
             if constexpr (MASKED) {
               const int key0 = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
               ds.x = (bits >> key0) & 1ull ? ds.x : 0.f;
@@ -382,11 +387,15 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     // one barrier per tile (loads landed; other buffer free for the next DMA).
-    // Wave 1 brought the tile's 64 lse values, one per lane: it takes them to
-    // log2 units in place before the barrier publishes them, once per query
-    // instead of once per (query, key) element below.
+    // Wave 1 brought the tile's 64 lse and D values, one of each per lane: it
+    // takes lse to log2 units and negates D in place before the barrier
+    // publishes them, once per query instead of once per (query, key) element
+    // below; the dP chains start from -D and deliver dP - D.
     wait_vmcnt<0>();
-    if (wave == 1) s.rowv[buf][0][lane] *= kLog2e;
+    if (wave == 1) {
+      s.rowv[buf][0][lane] *= kLog2e;
+      s.rowv[buf][1][lane] = -s.rowv[buf][1][lane];
+    }
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, qt_n);
     const uint16_t* Qt = s.t[buf][0];
@@ -396,9 +405,11 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     // blocks qb; lane holds queries 16qb + 4g + r of key j16)
     f32x4_t S[4], dP[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 4; ++qb) {
+      dP[qb] = *(const f32x4_t*)(&s.rowv[buf][1][16 * qb + 4 * g]);  // -D of the lane's queries
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[qb][r] = dP[qb][r] = 0.f;
+      for (int r = 0; r < 4; ++r) S[qb][r] = 0.f;
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8_t qop[4], dop[4];
@@ -423,7 +434,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
         const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][16 * qb + 4 * g]);
-        const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][16 * qb + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
           f32x2_t pv, ds;
@@ -433,8 +443,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
             pv.x = (bits >> (16 * qb + r)) & 1ull ? pv.x : 0.f;
             pv.y = (bits >> (16 * qb + r + 1)) & 1ull ? pv.y : 0.f;
           }
-          ds.x = pv.x * (dP[qb][r] - del4[r]);
-          ds.y = pv.y * (dP[qb][r + 1] - del4[r + 1]);
+          ds.x = pv.x * dP[qb][r];
+          ds.y = pv.y * dP[qb][r + 1];
           const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
           const bf16x2_t db2 = __builtin_convertvector(ds, bf16x2_t);
           const int slot = 4 * (qb & 1) + r;
@@ -614,11 +624,15 @@ void attn_bwd_dkdv32_kernel(BwdArgs a) {
       }
     }
     // one barrier per tile (loads landed; other buffer free for the next DMA).
-    // Wave 1 brought the tile's 64 lse values, one per lane: it takes them to
-    // log2 units in place before the barrier publishes them, once per query
-    // instead of once per (query, key) element below.
+    // Wave 1 brought the tile's 64 lse and D values, one of each per lane: it
+    // takes lse to log2 units and negates D in place before the barrier
+    // publishes them, once per query instead of once per (query, key) element
+    // below; the dP chains start from -D and deliver dP - D.
     wait_vmcnt<0>();
-    if (wave == 1) s.rowv[buf][0][lane] *= kLog2e;
+    if (wave == 1) {
+      s.rowv[buf][0][lane] *= kLog2e;
+      s.rowv[buf][1][lane] = -s.rowv[buf][1][lane];
+    }
     __syncthreads();
     if (e_n < e1) prefetch(buf ^ 1, en_n, qt_n);
     const bool part = en.pidx >= 0;  // uniform: only partial tiles test the row mask
@@ -629,9 +643,16 @@ void attn_bwd_dkdv32_kernel(BwdArgs a) {
 #pragma unroll 1
     for (int qb = 0; qb < BN / 32; ++qb) {
       // S = Q K^T and dP = dO V^T for 32 queries (lane = key)
+      // dP starts from -D of the lane's queries qb*32 + 8*(r/4) + 4*hi + r%4
       f32x16_t S, dP;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t nd4 = *(const f32x4_t*)(&s.rowv[buf][1][qb * 32 + 8 * i + 4 * hi]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dP[4 * i + t] = nd4[t];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = qb * 32 * D + koff[kk];
@@ -641,7 +662,7 @@ void attn_bwd_dkdv32_kernel(BwdArgs a) {
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dop, Vr[kk], dP, 0, 0, 0);
       }
       // lane holds queries qb*32 + 8*(r/4) + 4*hi + r%4 of its key; their
-      // lse and D come from LDS, four consecutive queries per read
+      // lse come from LDS, four consecutive queries per read
       bf16x8_t P[2], DS[2];
       auto make_p_ds = [&](auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -649,7 +670,6 @@ void attn_bwd_dkdv32_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int q0 = qb * 32 + 8 * i + 4 * hi;
           const f32x4_t lse4 = *(const f32x4_t*)(&s.rowv[buf][0][q0]);
-          const f32x4_t del4 = *(const f32x4_t*)(&s.rowv[buf][1][q0]);
 #pragma unroll
           for (int t = 0; t < 4; t += 2) {
             const int r = 4 * i + t;
@@ -660,8 +680,8 @@ void attn_bwd_dkdv32_kernel(BwdArgs a) {
               pv.x = (bits >> (q0 + t)) & 1ull ? pv.x : 0.f;
               pv.y = (bits >> (q0 + t + 1)) & 1ull ? pv.y : 0.f;
             }
-            ds.x = pv.x * (dP[r] - del4[t]);
-            ds.y = pv.y * (dP[r + 1] - del4[t + 1]);
+            ds.x = pv.x * dP[r];
+            ds.y = pv.y * dP[r + 1];
             const bf16x2_t pb = __builtin_convertvector(pv, bf16x2_t);
             const bf16x2_t d2 = __builtin_convertvector(ds, bf16x2_t);
             // value step st = i / 2 takes rows 16 st .. 16 st + 15, slots 4 (i % 2) + t
