@@ -18,12 +18,15 @@ constexpr int kTileN = 64;
 constexpr int kTileMWide = 256;
 
 // Which tangents a (query tile, key tile) pair carries, from the caller's
-// declaration of tokens whose tangents are zero (Entry::flags):
+// declaration of tokens whose tangents are zero (Entry::flags).  Only the
+// tokens taking part in the tile count: the keys that some query of the tile
+// may attend, and the queries attending one of them (a masked pair has P = 0
+// and its tS is set to 0, whatever the tangents).
 //   kTileJvp       the general case: every product of the JVP
-//   kTileKeysFree  tK = tV = 0 on every key of the tile: tS = c tQ K^T and
+//   kTileKeysFree  tK = tV = 0 on every taking-part key: tS = c tQ K^T and
 //                  (A + B) gets only (P.tS) V
-//   kTileAllFree   tQ = tK = tV = 0 for the whole tile: tS = 0, so only the
-//                  primal products remain
+//   kTileAllFree   tQ = tK = tV = 0 on every taking-part token: tS = 0, so only
+//                  the primal products remain
 // A query-tangent-free tile whose keys carry tangents runs as kTileJvp (tQ is
 // zero there and simply multiplies in).
 constexpr int32_t kTileJvp = 0;

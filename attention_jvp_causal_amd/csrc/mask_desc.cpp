@@ -79,6 +79,17 @@ bool covered(const std::vector<int32_t>& r, int32_t a, int32_t b) {
 }
 
 // Relative cost of one tile of each variant (units of 4d FLOP per pair).
+// Variant of a partial tile from the tokens that take part in it: the keys of
+// bitmask `keys` (key `key0 + j` for bit j) and whether every row attending one
+// of them is tangent-free.  Masked pairs contribute nothing (P = 0, tS is
+// set to 0), so the tangents of keys and rows outside the mask do not matter.
+int32_t partial_variant(const std::vector<int32_t>& tfree, uint64_t keys, int32_t key0, bool rows_free) {
+  bool keys_free = true;
+  for (int j = 0; j < 64 && keys_free; ++j)
+    if ((keys >> j) & 1ull) keys_free = covered(tfree, key0 + j, key0 + j + 1);
+  return keys_free ? (rows_free ? kTileAllFree : kTileKeysFree) : kTileJvp;
+}
+
 int64_t tile_cost(int32_t flags) { return flags == kTileJvp ? 3 : flags == kTileKeysFree ? 2 : 1; }
 int var_index(int32_t flags) { return flags == kTileJvp ? 0 : flags == kTileKeysFree ? 1 : 2; }
 
@@ -128,8 +139,9 @@ static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const
   m->bm = BM;
   m->n_qt = (Lo + BM - 1) / BM;
   m->n_kt = (Lv + BN - 1) / BN;
-  // tangent-free owner and visited tiles: every token of the tile inside
-  // the sequence is declared tangent-free
+  // tangent-free owner and visited tiles of full runs: every token of the
+  // tile inside the sequence is declared tangent-free (in a full tile every
+  // row attends every key); partial tiles decide from their bitmasks below
   auto q_free = [&](int32_t qt) { return covered(tfree, qt * BM, std::min(Lo, qt * BM + BM)); };
   auto k_free = [&](int32_t kt) { return covered(tfree, kt * BN, std::min(Lv, kt * BN + BN)); };
   auto variant = [&](bool qf, int32_t kt) {
@@ -204,8 +216,6 @@ static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const
       } else {
         for (int32_t kt = s0; kt < e1; ++kt) {
           const int32_t pidx = m->partial_tiles++;
-          const int32_t fl = variant(qf, kt);
-          m->entries.push_back(Entry{kt, kt + 1, pidx, fl});
           m->bits.resize(size_t(m->partial_tiles) * BM, 0);
           uint64_t* rowbits = &m->bits[size_t(pidx) * BM];
           const int32_t key0 = kt * BN;
@@ -217,7 +227,15 @@ static void build_map(int32_t Lo, int32_t Lv, const int32_t* r, int32_t n, const
             for (int32_t q = std::max(a, x.q0); q < std::min(b, x.q1); ++q) rowbits[q - a] |= msk;
           }
           int64_t c = 0;
-          for (int32_t row = 0; row < BM; ++row) c += __builtin_popcountll(rowbits[row]);
+          uint64_t keys = 0;  // keys that some row of the tile may attend
+          bool rows_free = true;  // every row that attends one of them is tangent-free
+          for (int32_t row = 0; row < BM; ++row) {
+            c += __builtin_popcountll(rowbits[row]);
+            keys |= rowbits[row];
+            if (rowbits[row] && rows_free) rows_free = covered(tfree, a + row, a + row + 1);
+          }
+          const int32_t fl = partial_variant(tfree, keys, key0, rows_free);
+          m->entries.push_back(Entry{kt, kt + 1, pidx, fl});
           m->pairs_by_var[var_index(fl)] += c;
         }
       }

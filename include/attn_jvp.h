@@ -161,9 +161,12 @@ int32_t attn_jvp_mask_desc_upload(aj_mask_desc* desc, int32_t device);
  * and dtype.  By passing it to attn_jvp_fwd the caller declares that tq, tk
  * and tv are exactly zero at these tokens (for every batch and head); the
  * kernel then skips the products that are zero, per tile of 128 queries x 64
- * keys that lies entirely inside the ranges, and need not read those
- * tangents.  Query tiles left with only primal work (all the tiles they visit
- * lie inside the ranges) run the primal forward of attn_fwd, which writes
+ * keys, and need not read those tangents.  A tile's keys count as
+ * tangent-free when every key that some query of the tile may attend lies
+ * inside the ranges, and its queries when every query attending one of those
+ * keys does (masked pairs contribute nothing, whatever their tangents).
+ * Query tiles left with only primal work (queries and keys tangent-free in
+ * every tile they visit) run the primal forward of attn_fwd, which writes
  * tO = 0 for them, in a launch of their own before the JVP kernel's.  The
  * result equals attn_jvp_fwd with the plain descriptor whenever the
  * declaration holds: bit for bit, except that O and lse of the primal-only

@@ -22,25 +22,25 @@ def _free_tokens(L, ranges):
     return free
 
 
-def _tile_free(free, t, size):
-    L = free.shape[0]
-    return bool(free[t * size:min(L, t * size + size)].all())
-
-
 def _expected(dm, free):
-    """(variant per visited tile, pairs per class) from a dense mask."""
+    """(variant per visited tile, pairs per class) from a dense mask.  A tile's
+    variant is decided by the tokens that take part in it: the keys that some
+    query of the tile may attend, and the queries that attend one of them
+    (masked pairs contribute nothing, whatever their tangents)."""
     L = dm.shape[0]
     nq, nk = -(-L // TM), -(-L // TN)
     var = {}
     pairs = [0, 0, 0]
     for qt in range(nq):
-        qf = _tile_free(free, qt, TM)
         block = dm[qt * TM:(qt + 1) * TM]
         for kt in range(nk):
-            cnt = int(block[:, kt * TN:(kt + 1) * TN].sum())
+            sub = block[:, kt * TN:(kt + 1) * TN]
+            cnt = int(sub.sum())
             if cnt == 0:
                 continue
-            kf = _tile_free(free, kt, TN)
+            keys = kt * TN + np.flatnonzero(sub.any(axis=0))
+            rows = qt * TM + np.flatnonzero(sub.any(axis=1))
+            kf, qf = bool(free[keys].all()), bool(free[rows].all())
             v = 3 if (qf and kf) else (1 if kf else 0)
             var[(qt, kt)] = v
             pairs[{0: 0, 1: 1, 3: 2}[v]] += cnt
@@ -88,7 +88,10 @@ def test_variants_and_pair_counts_exhaustive(mask, ranges, head_dim):
 
 def test_teacher_forcing_full_size_clean_context():
     # packed [clean | noisy] at the Wan2.1 shape, clean tokens declared
-    # tangent-free: per-class pair counts from per-row key ranges
+    # tangent-free: per-class pair counts from per-row key ranges, tile by
+    # tile (the rows of a query tile fall into a few groups with the same key
+    # ranges; per group and key tile, the allowed keys and how many of them
+    # carry a tangent follow from prefix counts)
     T, F = 21, 1560
     m = MaskLayout("tf_clean_noisy", T, F, 1)
     L, half = m.seq_len, T * F
@@ -96,17 +99,28 @@ def test_teacher_forcing_full_size_clean_context():
     d = aj.attn_jvp_mask_desc_tangent_free(base, [(0, half)])
     free = _free_tokens(L, [(0, half)])
     nk = -(-L // TN)
-    kfree = np.array([_tile_free(free, kt, TN) for kt in range(nk)])
-    key_in_free_tile = np.repeat(kfree, TN)[:L]
-    C = np.concatenate([[0], np.cumsum(key_in_free_tile)])
+    k0s = np.arange(nk) * TN
+    k1s = np.minimum(k0s + TN, L)
+    NF = np.concatenate([[0], np.cumsum(~free)])  # keys carrying a tangent before index
     pairs = [0, 0, 0]
-    qfree = [_tile_free(free, qt, TM) for qt in range(-(-L // TM))]
-    for i in range(L):
-        qf = qfree[i // TM]
-        for a, b in key_ranges(m, i):
-            nf = int(C[b] - C[a])
-            pairs[0] += (b - a) - nf
-            pairs[2 if qf else 1] += nf
+    for qt in range(-(-L // TM)):
+        groups = {}
+        for i in range(qt * TM, min(L, qt * TM + TM)):
+            groups.setdefault(tuple(key_ranges(m, i)), []).append(i)
+        allowed = np.zeros(nk, np.int64)        # allowed pairs per key tile
+        tangent_keys = np.zeros(nk, np.int64)   # allowed keys carrying a tangent (summed over groups)
+        tangent_rows = np.zeros(nk, bool)       # some attending row carries a tangent
+        for rng, rows in groups.items():
+            per_row = np.zeros(nk, np.int64)
+            for a, b in rng:
+                lo, hi = np.maximum(a, k0s), np.minimum(b, k1s)
+                per_row += np.clip(hi - lo, 0, None)
+                tangent_keys += np.where(hi > lo, NF[np.maximum(hi, lo)] - NF[lo], 0)
+            allowed += per_row * len(rows)
+            tangent_rows |= (per_row > 0) & (not free[rows].all())
+        for kt in np.flatnonzero(allowed):
+            kf, rf = tangent_keys[kt] == 0, not tangent_rows[kt]
+            pairs[2 if (kf and rf) else 1 if kf else 0] += int(allowed[kt])
     assert list(d.work()) == pairs
     assert sum(pairs) == unmasked_pairs(m) == 1_124_323_200
     # the clean half is mostly primal-only work; noisy queries over clean keys

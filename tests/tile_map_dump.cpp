@@ -6,10 +6,14 @@
 //
 // stdin: "R q_len kv_len n" and n rectangles q0 q1 k0 k1, or
 // "L kind num_frames frame_tokens frames_per_chunk" (a frame-level layout,
-// expanded by the library into rectangles).
-// stdout, per map: "M rows n_qt n_kt", then per entry "E qt kt0 kt1 pidx"
-// followed, for a partial tile, by its per-row bitmasks (hex, one per row),
-// then "T" and the task order.
+// expanded by the library into rectangles); then optionally "F n" and n
+// tangent-free token ranges t0 t1.
+// stdout, per map (query tiles of 128 rows, of 256 rows, then the transposed
+// map of 128-key tiles): "M rows n_qt n_kt", then per entry
+// "E qt kt0 kt1 pidx flags" followed, for a partial tile, by its per-row
+// bitmasks (hex, one per row), then "T" and the task order, and for a map
+// with primal-only tiles "S n_primal" and the split task order.
+// On a builder error: "ERR status", exit code 1.
 #include <cstdio>
 #include <vector>
 
@@ -33,18 +37,28 @@ int main() {
     for (int32_t& x : r)
       if (std::scanf("%d", &x) != 1) return 2;
   }
+  std::vector<int32_t> tf;
+  char f = 0;
+  if (std::scanf(" %c", &f) == 1) {
+    int n_tf = 0;
+    if (f != 'F' || std::scanf("%d", &n_tf) != 1 || n_tf < 0) return 2;
+    tf.resize(2 * size_t(n_tf));
+    for (int32_t& x : tf)
+      if (std::scanf("%d", &x) != 1) return 2;
+  }
   aj_mask_desc* d = nullptr;
-  const int32_t st = aj::build_from_rects(lq, lk, r.data(), int32_t(r.size() / 4), 128, AJ_BF16, nullptr, 0, &d);
+  const int32_t st = aj::build_from_rects(lq, lk, r.data(), int32_t(r.size() / 4), 128, AJ_BF16, tf.data(),
+                                          int32_t(tf.size() / 2), &d);
   if (st != AJ_OK) {
     std::printf("ERR %d\n", st);
     return 1;
   }
-  for (const aj::TileMap* m : {&d->rows, &d->rows_w}) {
+  for (const aj::TileMap* m : {&d->rows, &d->rows_w, &d->cols}) {
     std::printf("M %d %d %d\n", m->bm, m->n_qt, m->n_kt);
     for (int32_t qt = 0; qt < m->n_qt; ++qt)
       for (int32_t e = m->qt_off[qt]; e < m->qt_off[qt + 1]; ++e) {
         const aj::Entry& x = m->entries[e];
-        std::printf("E %d %d %d %d\n", qt, x.kt0, x.kt1, x.pidx);
+        std::printf("E %d %d %d %d %d\n", qt, x.kt0, x.kt1, x.pidx, x.flags);
         if (x.pidx >= 0)
           for (int32_t row = 0; row < m->bm; ++row)
             std::printf("%llx\n", static_cast<unsigned long long>(m->bits[size_t(x.pidx) * m->bm + row]));
@@ -52,6 +66,11 @@ int main() {
     std::printf("T");
     for (int32_t t : m->tasks) std::printf(" %d", t);
     std::printf("\n");
+    if (!m->tasks_split.empty()) {
+      std::printf("S %d", m->n_primal_tasks);
+      for (int32_t t : m->tasks_split) std::printf(" %d", t);
+      std::printf("\n");
+    }
   }
   delete d;
   return 0;
