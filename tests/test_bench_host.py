@@ -99,3 +99,24 @@ def test_traffic_records_match_the_kernel_code():
         assert rec["kernel"] == bench.kernel_name(w.dtype, w.head_dim, False, scale=w.scale), path
         assert rec["kernel_isa"] == bench.kernel_isa_sha(rec["kernel"]), path
         assert bench.measured_traffic(w.name) == rec["bytes_per_launch"] > 0, path
+
+
+def test_counter_profiles_name_the_kernel_code_that_builds():
+    # every profiles/*.md names the code hash of the kernel it measured; it
+    # must be the hash of a kernel this build produces (re-profile after a
+    # change to a kernel's code), and its title must name that kernel
+    import glob
+    import re
+
+    with open(os.path.join(ROOT, "attention_jvp_causal_amd", "libattnjvp.isa.json")) as f:
+        isa = json.load(f)
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert paths
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        m = re.search(r"Kernel code hash.*?\): `([0-9a-f]{16})`", text)
+        assert m, path
+        title = re.match(r"# `([^`]+)`", text).group(1)
+        names = [k for k, v in isa.items() if v == m.group(1)]
+        assert any(f"aj::{title}(" in k for k in names), (path, title, m.group(1))
