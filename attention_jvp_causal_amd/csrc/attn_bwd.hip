@@ -22,12 +22,13 @@
 //   lane column, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly,
 //   dO^T and Q^T coming from transpose reads.
 // dQ runs 4 waves of 32 rows (v_mfma_f32_32x32x16_bf16, two workgroups per
-// CU at d = 128, three at d = 64), dK / dV waves of 16 keys
-// (v_mfma_f32_16x16x32_bf16; 8 per workgroup and two waves per SIMD at
-// d = 128, 4 per workgroup and three per SIMD at d = 64); both use the direct
-// buffer -> LDS DMA into a double buffer and the
-// swizzled tile layouts of the forward kernels.  Masked pairs are removed by select
-// (P = dS = 0), never by arithmetic on -inf.
+// CU at d = 128, three at d = 64).  dK / dV runs 8 waves of 16 keys at
+// d = 128 (v_mfma_f32_16x16x32_bf16, two waves per SIMD) and 4 waves of 32
+// keys at d = 64 (v_mfma_f32_32x32x16_bf16, two workgroups per CU).  All use
+// the direct buffer -> LDS DMA into a double buffer and the swizzled tile
+// layouts of the forward kernels.  The dP chains start from -D, so the MFMAs
+// deliver dP - D.  Masked pairs are removed by select (P = dS = 0), never by
+// arithmetic on -inf.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
