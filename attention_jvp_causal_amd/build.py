@@ -38,6 +38,10 @@ def hipcc() -> str:
 # LLVM's iterative ILP scheduler than under the default (same-box A/B, both head
 # dims) and still spill nothing. The 32-row forward kernels gain about as much but
 # spill under it, and the 16-row JVP kernel gains nothing: both keep the default.
+# The iterative min-register strategy spills nowhere but ran every forward
+# kernel 1-7 % slower (the 16-row JVP 7 %); the AMDGPU register-pressure
+# trackers and a latency-only schedule metric leave the plain kernels' code as
+# it is.
 SOURCE_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
