@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
     L.attn_jvp_mask_desc_work.argtypes = [pdesc, ctypes.POINTER(i64)]
     L.attn_jvp_mask_desc_tile_variant.argtypes = [pdesc, i32, i32, ctypes.POINTER(i32)]
     L.attn_jvp_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P]
+    L.attn_jvp_fwd_v16.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P, P, P]
     L.attn_fwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, pdesc, f32, P, P, P]
     L.attn_bwd.argtypes = [ctypes.POINTER(aj_shape), P, P, P, P, P, P, pdesc, f32, P, P, P, P, P]
     L.attn_fwd_kv.argtypes = [ctypes.POINTER(aj_kv_shape), P, P, P, pdesc, f32, P, P, P]
@@ -103,7 +104,8 @@ def lib() -> ctypes.CDLL:
                "attn_jvp_mask_desc_tile_kind", "attn_jvp_mask_desc_row_bits", "attn_jvp_fwd",
                "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_work", "attn_jvp_mask_desc_tile_variant",
                "attn_fwd", "attn_bwd", "attn_jvp_mask_desc_col_bits", "attn_fwd_kv",
-               "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_mask_desc_upload", "attn_bwd_noalloc"):
+               "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_mask_desc_upload", "attn_bwd_noalloc",
+               "attn_jvp_fwd_v16"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -367,6 +369,31 @@ def attn_jvp_fwd(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = N
     return o, to, lse
 
 
+def attn_jvp_fwd_v16(q, k, v, tq, tk, tv, mask: MaskDesc, scale: Optional[float] = None,
+                     out_dtype=None, out: Optional[Tuple] = None, v16: Optional[Tuple] = None, stream=None):
+    """attn_jvp_fwd at head_dim 64 (bf16 inputs) through fp16 copies of v and tv
+    that the call writes first into ``v16`` = (v16, tv16): float16 tensors of
+    v's shape and strides (allocated here when not given).  Same results as
+    attn_jvp_fwd, bit for bit.  Returns (o, to, lse)."""
+    import torch
+
+    ins = (q, k, v, tq, tk, tv)
+    sh, (o, to), lse, scale = _prepare(ins, out_dtype, scale, out, 2)
+    if v16 is None:
+        v16 = tuple(torch.empty_like(v, dtype=torch.float16) for _ in range(2))
+    if len(v16) != 2 or any(t.dtype != torch.float16 or t.shape != v.shape or t.stride() != v.stride()
+                            or t.device != v.device for t in v16):
+        raise ValueError("v16 must hold two float16 tensors with v's shape, strides and device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().attn_jvp_fwd_v16(ctypes.byref(sh), *(t.data_ptr() for t in ins), mask.handle, scale,
+                                    o.data_ptr(), to.data_ptr(), lse.data_ptr(), v16[0].data_ptr(),
+                                    v16[1].data_ptr(), ctypes.c_void_p(stream))
+    _check(st, "attn_jvp_fwd_v16")
+    return o, to, lse
+
+
 def attn_fwd(q, k, v, mask: MaskDesc, scale: Optional[float] = None, out_dtype=None,
              out: Optional[Tuple] = None, stream=None):
     """O, lse of masked attention (primal forward, bf16 inputs) on the GPU.
@@ -499,6 +526,7 @@ __all__ = [
     "AJ_OK", "AJ_EINVAL", "AJ_ENOTSUP", "AJ_ENOMEM", "AJ_EHIP", "AJ_EMASK", "AJ_ENOTLOADED", "AJ_F32", "AJ_BF16",
     "AttnJvpError", "MaskDesc", "lib", "status_str", "attn_jvp_version", "attn_jvp_mask_desc_build",
     "attn_jvp_mask_desc_from_rects", "attn_jvp_mask_desc_tangent_free", "attn_jvp_mask_desc_free",
-    "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_noalloc",
+    "attn_jvp_mask_desc_from_rects_kv", "attn_jvp_fwd", "attn_jvp_fwd_v16", "attn_fwd", "attn_fwd_kv", "attn_bwd",
+    "attn_bwd_noalloc",
     "LIB_PATH",
 ]

@@ -226,6 +226,12 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 // resolution (2^-24) and larger ones saturate to 65504 (round toward zero).
 // Called after the wave's own DMA has landed (vmcnt 0) and before the barrier
 // that publishes the buffer, so no other wave reads these chunks meanwhile.
+// One 32-bit pair of bf16 values (low half first) as a pair of fp16 values.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
 template <int NW, int D, int NTEN>
 __device__ __forceinline__ void bf16_chunks_to_f16(uint16_t* t0, uint16_t* t1, int wave, int lane) {
   constexpr int NI = TileLoadPlan<NW, D>::NI;
@@ -235,10 +241,7 @@ __device__ __forceinline__ void bf16_chunks_to_f16(uint16_t* t0, uint16_t* t1, i
     const u32x4_t x = *(const u32x4_t*)p;
     u32x4_t y;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float lo = __uint_as_float(x[w] << 16), hi = __uint_as_float(x[w] & 0xffff0000u);
-      y[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-    }
+    for (int w = 0; w < 4; ++w) y[w] = bf16x2_to_f16x2(x[w]);
     *(u32x4_t*)p = y;
   }
 }

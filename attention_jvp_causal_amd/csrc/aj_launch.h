@@ -32,6 +32,11 @@ struct FwdArgs {
   const int32_t* tasks;
   const uint64_t* bits;
   int32_t tile_m;  // query rows per task: kTileM, or kTileMWide (the primal forward's wide map)
+  // the JVP at d = 64 only: caller-owned buffers with the key strides that
+  // receive fp16 copies of v and tv before the kernel reads them; null: the
+  // kernel converts each key tile in LDS
+  void* v16;
+  void* tv16;
 };
 
 // Arguments of the gradient kernels (bf16 inputs [B, H, L, D] sharing the
@@ -77,7 +82,10 @@ void launch_q16(const FwdArgs& a, bool out_f32, bool variants, dim3 grid, hipStr
 // Enqueues the forward kernel; returns an aj_status.  jvp = false computes
 // only O and lse (tq, tk, tv and to are not used).  variants = true when the
 // descriptor declares tangent-free tiles: the kernel instance that skips
-// their zero products runs instead of the plain one.
+// their zero products runs instead of the plain one.  a.v16 non-null (the
+// bf16 JVP at head_dim 64 only, else AJ_ENOTSUP): a conversion kernel first
+// writes fp16 copies of v and tv to a.v16 and a.tv16, which the JVP kernel
+// then reads instead of converting every key tile in LDS.
 int launch_fwd(FwdArgs a, int in_dtype, int out_dtype, int head_dim, bool jvp, bool variants,
                hipStream_t stream);
 

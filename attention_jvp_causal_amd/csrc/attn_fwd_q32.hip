@@ -70,11 +70,18 @@ constexpr int q32_waves_per_simd() { return D == 64 && !JVP ? 3 : 2; }
 // run them.  Tiles where neither queries nor keys carry tangents take the same
 // keys-tangent-free path: their tQ is zero, so their score tangents and u are
 // exact zeros.
-template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false, bool VARIANTS = false, int NWV = kWavesQ32>
+//
+// V16 (JVP at d = 64 only): V and tV come as fp16 copies made by
+// bf16_to_f16_kv_kernel before the launch (a.v16, a.tv16, with the key
+// strides), so the per-tile conversion in LDS is skipped; the values are the
+// same, so are the results, bit for bit.
+template <int D, bool OUT_F32, bool JVP, bool SCALE_IN_Q = false, bool VARIANTS = false, int NWV = kWavesQ32,
+          bool V16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV),
                           amdgpu_waves_per_eu(q32_waves_per_simd<D, JVP>(), q32_waves_per_simd<D, JVP>())))
 void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   static_assert(NWV == kWavesQ32 || (NWV == 8 && D == 128 && !JVP), "8-wave workgroups: d = 128 primal only");
+  static_assert(!V16 || (JVP && D == 64), "fp16 copies of V and tV: the JVP at d = 64 only");
   constexpr int NKK = D / 16;  // MFMA k-steps over d for the score products
   constexpr int NDB = D / 32;  // 32-row blocks of d for the value products
   constexpr int NT = JVP ? 4 : 2;
@@ -106,8 +113,10 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
   const int64_t kv_off = bb * a.ksb + hh * a.ksh;
   const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + in_off;
   const uint16_t* __restrict__ tQg = JVP ? (const uint16_t*)a.tq + in_off : nullptr;
+  const void* const vsrc = V16 ? a.v16 : a.v;
+  const void* const tvsrc = V16 ? a.tv16 : a.tv;
   const uint16_t* const src[4] = {(const uint16_t*)a.k + kv_off, JVP ? (const uint16_t*)a.tk + kv_off : nullptr,
-                                  (const uint16_t*)a.v + kv_off, JVP ? (const uint16_t*)a.tv + kv_off : nullptr};
+                                  (const uint16_t*)vsrc + kv_off, JVP ? (const uint16_t*)tvsrc + kv_off : nullptr};
   const int q_row = qt * BMW + wave * 32 + l32;
 
   const TileLoadPlan<NWV, D> plan(a.ksl, wave, lane, swz_q32<D>);
@@ -352,7 +361,7 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     // fp16 value products: this wave's share of the V and tV tiles, converted
     // before the barrier publishes them
-    if constexpr (F16) {
+    if constexpr (F16 && !V16) {
       if (!VARIANTS || en.flags == kTileJvp)
         bf16_chunks_to_f16<NWV, D, 2>(s.t[buf][Lds::slot(2)], s.t[buf][Lds::slot(3)], wave, lane);
       else
@@ -405,6 +414,31 @@ void attn_jvp_fwd_bf16_q32_kernel(FwdArgs a) {
     if (hi == 0)
       a.lse[(int64_t)bh * L + q_row] = l_tot > 0.f ? (m_run + kPScaleLog2 + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+}
+
+// fp16 copies of V and tV for the V16 instances: every row of every (b, h)
+// up to the key length, at the key strides, each 32-bit pair of bf16 values
+// rewritten by bf16x2_to_f16x2 (the conversion bf16_chunks_to_f16 applies in
+// LDS).  One thread per 16-byte chunk: threads [0, n) take V, [n, 2n) tV,
+// n = B * H * Lk * D / 8.
+template <int D>
+__global__ __launch_bounds__(256) void bf16_to_f16_kv_kernel(FwdArgs a) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  const int64_t n = int64_t(a.B) * a.H * a.Lk * CH;
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= 2 * n) return;
+  const bool t = i >= n;
+  if (t) i -= n;
+  const int c = int(i % CH);
+  const int64_t row = i / CH;  // (b * H + h) * Lk + l
+  const int64_t l = row % a.Lk, bh = row / a.Lk;
+  const int64_t b = bh / a.H, h = bh - b * a.H;
+  const int64_t off = b * a.ksb + h * a.ksh + l * a.ksl + 8 * c;
+  const u32x4_t x = *(const u32x4_t*)((const uint16_t*)(t ? a.tv : a.v) + off);
+  u32x4_t y;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) y[w] = bf16x2_to_f16x2(x[w]);
+  *(u32x4_t*)((uint16_t*)(t ? a.tv16 : a.v16) + off) = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -613,6 +647,24 @@ static void launch_bf16(const FwdArgs& a, bool out_f32, int head_dim, dim3 grid,
     int e2 = 0;
     const bool pow2 = a.scale > 0.f && a.scale <= 1.f && std::frexp(a.scale, &e2) == 0.5f;
     if constexpr (JVP) {
+      if (a.v16) {  // V and tV converted by bf16_to_f16_kv_kernel, launched just before
+        if (pow2) {
+          if (out_f32)
+            hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true, VARIANTS, kWavesQ32, true>), grid, b32,
+                               0, stream, a);
+          else
+            hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, VARIANTS, kWavesQ32, true>), grid, b32,
+                               0, stream, a);
+        } else {
+          if (out_f32)
+            hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, false, VARIANTS, kWavesQ32, true>), grid, b32,
+                               0, stream, a);
+          else
+            hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, VARIANTS, kWavesQ32, true>), grid,
+                               b32, 0, stream, a);
+        }
+        return;
+      }
       if (pow2) {
         if (out_f32)
           hipLaunchKernelGGL((attn_jvp_fwd_bf16_q32_kernel<64, true, true, true, VARIANTS>), grid, b32, 0, stream, a);
@@ -632,6 +684,14 @@ int launch_fwd(FwdArgs a, int in_dtype, int out_dtype, int head_dim, bool jvp, b
   if (grid64 <= 0 || grid64 > 0x7fffffff) return AJ_EINVAL;
   a.head_group = head_group_for(a.B * a.H);
   const dim3 grid((unsigned)grid64);
+  if (a.v16 && !(jvp && in_dtype == AJ_BF16 && head_dim == 64)) return AJ_ENOTSUP;
+  if (a.v16) {
+    // fp16 copies of V and tV for the d = 64 JVP, in stream order before it
+    const int64_t threads = 2 * int64_t(a.B) * a.H * a.Lk * (64 / 8);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff) return AJ_EINVAL;
+    hipLaunchKernelGGL(bf16_to_f16_kv_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
   if (in_dtype == AJ_BF16) {
     if (!jvp) launch_bf16<false, false>(a, out_dtype == AJ_F32, head_dim, grid, stream);
     else if (variants) launch_bf16<true, true>(a, out_dtype == AJ_F32, head_dim, grid, stream);

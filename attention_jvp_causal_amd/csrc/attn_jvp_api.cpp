@@ -354,15 +354,22 @@ void attn_jvp_mask_desc_free(aj_mask_desc* d) {
   delete d;
 }
 
-int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq,
-                     const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
-                     void* to, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// attn_jvp_fwd, and attn_jvp_fwd_v16 when v16 and tv16 are given (checked by
+// the caller).
+int32_t jvp_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                const void* tv, const aj_mask_desc* mask, float scale, void* o, void* to, float* lse, void* v16,
+                void* tv16, void* stream) {
   const void* ins[6] = {q, k, v, tq, tk, tv};
   const void* outs[3] = {o, to, lse};
   aj::FwdArgs a;
   int32_t st = prepare(s, ins, 6, outs, 3, mask, scale, &a);
   if (st != AJ_OK) return st;
   a.tq = tq; a.tk = tk; a.tv = tv; a.to = to;
+  a.v16 = v16; a.tv16 = tv16;
   const bool variants = mask->rows.pairs_by_var[1] + mask->rows.pairs_by_var[2] > 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (!variants || s->in_dtype != AJ_BF16)
@@ -379,6 +386,7 @@ int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void
     aj::FwdArgs p = a;
     p.tasks = t->rows.tasks_split;
     p.n_tasks = np;
+    p.v16 = p.tv16 = nullptr;  // the primal kernel reads V in bf16
     st = aj::launch_fwd(p, s->in_dtype, s->out_dtype, s->head_dim, false, false, hs);
     if (st != AJ_OK) return st;
   }
@@ -389,6 +397,24 @@ int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void
     st = aj::launch_fwd(r, s->in_dtype, s->out_dtype, s->head_dim, true, variants, hs);
   }
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_jvp_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq,
+                     const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
+                     void* to, float* lse, void* stream) {
+  return jvp_fwd(s, q, k, v, tq, tk, tv, mask, scale, o, to, lse, nullptr, nullptr, stream);
+}
+
+int32_t attn_jvp_fwd_v16(const aj_shape* s, const void* q, const void* k, const void* v, const void* tq,
+                         const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
+                         void* to, float* lse, void* v16, void* tv16, void* stream) {
+  if (!v16 || !tv16 || !aligned16(v16) || !aligned16(tv16)) return AJ_EINVAL;
+  if (s && (s->head_dim != 64 || s->in_dtype != AJ_BF16)) return AJ_ENOTSUP;  // before any device work
+  return jvp_fwd(s, q, k, v, tq, tk, tv, mask, scale, o, to, lse, v16, tv16, stream);
 }
 
 int32_t attn_fwd(const aj_shape* s, const void* q, const void* k, const void* v, const aj_mask_desc* mask,

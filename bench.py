@@ -21,6 +21,11 @@ Other measurements of the same kernels (one JSON line each, same schema):
                    queries over the whole sequence's keys held as a cache
                    (block-causal workloads): 4d FLOP per pair.
 
+At head_dim 64 the JVP step is attn_jvp_fwd_v16 (a conversion kernel writes
+fp16 copies of V and tV into buffers allocated before the timed steps, then
+the JVP kernel reads them; same results as attn_jvp_fwd, bit for bit);
+--no-v16 times attn_jvp_fwd instead.
+
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -59,9 +64,18 @@ def kernel_isa_sha(kernel: str):
     return isa.get(f"void aj::{kernel}(aj::FwdArgs)") or isa.get(f"void aj::{kernel}(aj::BwdArgs)")
 
 
+def uses_v16(dtype: str, head_dim: int, op: str = "jvp") -> bool:
+    """Whether bench.py runs the JVP through attn_jvp_fwd_v16 (fp16 copies of V
+    and tV made by a conversion kernel before the JVP kernel): the bf16 JVP at
+    head_dim 64, unless --no-v16."""
+    return op == "jvp" and dtype == "bf16" and head_dim == 64
+
+
 def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tangent_free: bool = False,
-                scale: float = None) -> str:
-    """Name of the kernel instance(s) the library launches for this call."""
+                scale: float = None, v16: bool = False) -> str:
+    """Name of the kernel instance(s) the library launches for this call, in
+    launch order; the last one is the kernel the roofline and the traffic
+    record describe."""
     b = lambda x: "true" if x else "false"
     o = b(out_f32)
     if op == "bwd":
@@ -69,32 +83,38 @@ def kernel_name(dtype: str, head_dim: int, out_f32: bool, op: str = "jvp", tange
         return f"attn_bwd_dq32_kernel<{head_dim}, {o}> + {dkdv}"
     if dtype == "f32":
         return f"attn_jvp_fwd_f32_kernel<{head_dim}>"
-    # the last template argument is the workgroup's wave count: the primal
+    # the last two template arguments: the workgroup's wave count (the primal
     # forward at d = 128 runs 8-wave (256-row) tasks, the primal-only tiles of
-    # a tangent-free JVP and every other q32 instance 4-wave (128-row) ones
-    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false, false, 4>"
+    # a tangent-free JVP and every other q32 instance 4-wave (128-row) ones),
+    # and whether V and tV come as fp16 copies
+    primal = f"attn_jvp_fwd_bf16_q32_kernel<{head_dim}, {o}, false, false, false, 4, false>"
     if op in ("fwd", "kv"):
-        return primal if head_dim == 64 else f"attn_jvp_fwd_bf16_q32_kernel<128, {o}, false, false, false, 8>"
+        return primal if head_dim == 64 else f"attn_jvp_fwd_bf16_q32_kernel<128, {o}, false, false, false, 8, false>"
     if head_dim == 128:
         jvp = f"attn_jvp_fwd_bf16_q16_kernel<128, {o}, {b(tangent_free)}>"
     else:
         s = 1.0 / math.sqrt(head_dim) if scale is None else scale
         m, _ = math.frexp(s)
-        jvp = f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}, {b(tangent_free)}, 4>"
+        jvp = (f"attn_jvp_fwd_bf16_q32_kernel<64, {o}, true, {b(0.0 < s <= 1.0 and m == 0.5)}, {b(tangent_free)}, 4, "
+               f"{b(v16)}>")
+        if v16:
+            jvp = f"bf16_to_f16_kv_kernel<64> + {jvp}"
     # a tangent-free descriptor runs its primal-only query tiles through the
     # primal kernel first
     return f"{primal} + {jvp}" if tangent_free else jvp
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the rocprofv3 counter runs recorded under
-    profiles/, or None if they were taken on other code than the kernel the
-    current build holds."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the rocprofv3 counter runs
+    recorded under profiles/, or None if they were taken on another kernel or
+    on other code than the kernel the current build holds."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("kernel") != kernel:
+        return None
     isa = kernel_isa_sha(rec.get("kernel", ""))
     if isa is None or rec.get("kernel_isa") != isa:
         return None
@@ -114,7 +134,8 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, calib_mib: int
     from attention_jvp_causal_amd.workloads import WORKLOADS
 
     w = WORKLOADS[workload]
-    kname = kernel_name(w.dtype, w.head_dim, False, scale=w.scale)
+    kname = kernel_name(w.dtype, w.head_dim, False, scale=w.scale,
+                        v16=uses_v16(w.dtype, w.head_dim)).split(" + ")[-1]
     kname_sym = kname.split("<")[0]
 
     def per_dispatch(path, counter):
@@ -262,6 +283,9 @@ def main(argv=None):
     ap.add_argument("--op", default="jvp", choices=["jvp", "fwd", "bwd", "kv"],
                     help="jvp: O, tO, lse (the metric); fwd: primal O, lse only; bwd: dq, dk, dv; "
                          "kv: last chunk over a KV cache")
+    ap.add_argument("--no-v16", action="store_true",
+                    help="JVP at head_dim 64: call attn_jvp_fwd (fp16 conversion per key tile in LDS) instead of "
+                         "attn_jvp_fwd_v16 (fp16 copies of V and tV made once by a conversion kernel)")
     ap.add_argument("--tangent-free", action="store_true",
                     help="declare the clean half of a teacher-forcing workload tangent-free")
     ap.add_argument("--clock-seconds", type=float, default=2.0,
@@ -329,6 +353,9 @@ def main(argv=None):
             torch.empty((B, H, L, D), dtype=odt, device="cuda:0"),
             torch.empty((B, H, L), dtype=torch.float32, device="cuda:0"))
     args_ = [dev[n] for n in ("q", "k", "v", "tq", "tk", "tv")]
+    v16 = uses_v16(w.dtype, w.head_dim, args.op) and not args.no_v16
+    if v16:  # the fp16 copy buffers, allocated once outside the timed steps
+        v16_bufs = tuple(torch.empty_like(dev[n], dtype=torch.float16) for n in ("v", "tv"))
 
     if args.op == "bwd":
         # forward outputs and a cotangent, made before the timed region
@@ -346,6 +373,8 @@ def main(argv=None):
     def step():
         if args.op == "kv":
             aj.attn_fwd_kv(q_chunk, dev["k"], dev["v"], desc, scale=w.scale, out_dtype=out_dtype, out=(o_kv, lse_kv))
+        elif args.op == "jvp" and v16:
+            aj.attn_jvp_fwd_v16(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs, v16=v16_bufs)
         elif args.op == "jvp":
             aj.attn_jvp_fwd(*args_, desc, scale=w.scale, out_dtype=out_dtype, out=outs)
         elif args.op == "fwd":
@@ -399,7 +428,8 @@ def main(argv=None):
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = exec_flop / (avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
-    traffic = measured_traffic(w.name)
+    kname = kernel_name(w.dtype, D, odt == torch.float32, args.op, args.tangent_free, w.scale, v16=v16)
+    traffic = measured_traffic(w.name, kname.split(" + ")[-1])
     n_in, n_out = {"jvp": (6, 2), "fwd": (3, 1), "bwd": (5, 3), "kv": (2, 0)}[args.op]
     in_bytes = n_in * B * H * L * D * inputs["q"].element_size() + (B * H * L * 4 if args.op == "bwd" else 0)
     out_bytes = n_out * B * H * L * D * odt.itemsize + B * H * L * 4
@@ -436,6 +466,8 @@ def main(argv=None):
             "flop_per_step": flop,
             "op": args.op,
             "kv_cache": (f"last chunk of {q_len} queries over {L} cached keys" if args.op == "kv" else None),
+            "v_tv_fp16_copies": ("attn_jvp_fwd_v16: a conversion kernel writes fp16 copies of V and tV, then the "
+                                 "JVP kernel reads them; both inside the timed step" if v16 else None),
             "tangent_free": ("clean half [0, L/2) declared tangent-free; value counts 12d per pair, "
                              "roofline the executed 12d / 8d / 4d per pair by tile class")
                             if args.tangent_free else None,
@@ -451,7 +483,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": kernel_name(w.dtype, D, odt == torch.float32, args.op, args.tangent_free, w.scale),
+            "kernel": kname,
             "launch_ms_avg": round(avg_ms, 4),
             "launch_ms_min": round(launch_ms[0], 4),
             "algorithmic_hbm_bytes": in_bytes + out_bytes,

@@ -257,6 +257,23 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
                      const void* tq, const void* tk, const void* tv, const aj_mask_desc* mask,
                      float scale, void* o, void* to, float* lse, void* stream);
 
+/* attn_jvp_fwd at head_dim 64 with bf16 inputs, for callers that can give it
+ * two buffers: v16 and tv16 are device buffers (16-byte aligned, owned by the
+ * caller, each covering every element of v at the input strides) that the
+ * call first fills with fp16 copies of v and tv, with the conversion the
+ * kernel otherwise applies to every key tile in its local memory (exact for
+ * magnitudes in [2^-14, 65504]; round toward zero below, saturation above);
+ * the JVP kernel then reads the copies.  Same operation as attn_jvp_fwd
+ * ("Causal-rCM", App. B, Eqs. 42-45), same results bit for bit, fewer
+ * instructions per key tile.  v16 and tv16 must not overlap each other or any
+ * other argument; their contents after the call are the copies.  Two kernels
+ * in stream order; allocates nothing.  Errors: those of attn_jvp_fwd;
+ * AJ_EINVAL for a null or misaligned v16 / tv16; AJ_ENOTSUP unless
+ * head_dim is 64 and in_dtype AJ_BF16. */
+int32_t attn_jvp_fwd_v16(const aj_shape* shape, const void* q, const void* k, const void* v, const void* tq,
+                         const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o, void* to,
+                         float* lse, void* v16, void* tv16, void* stream);
+
 /* Primal masked attention (Eq. 42): O = softmax(scale * Q K^T + M) V and lse,
  * the forward of the student's packed teacher-forcing attention (Sec. 3.1.1,
  * Eq. 8) on the same descriptor as the JVP.  Same shapes, strides and checks

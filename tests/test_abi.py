@@ -169,6 +169,35 @@ def test_fwd_rejects_bad_arguments_before_launch():
     assert _fwd(_shape(D=128), d64.handle) == E.AJ_EMASK
 
 
+def _fwd_v16(shape, desc, ptrs=None, scale=0.125, lse=FAKE, v16=FAKE + 4096, tv16=FAKE + 8192):
+    ptrs = ptrs or [FAKE] * 8
+    p = [ctypes.c_void_p(x) if x is not None else None for x in ptrs]
+    w = [ctypes.c_void_p(x) if x is not None else None for x in (v16, tv16)]
+    return aj.lib().attn_jvp_fwd_v16(ctypes.byref(shape) if shape is not None else None, *p[:6],
+                                     desc, ctypes.c_float(scale), p[6], p[7],
+                                     ctypes.c_void_p(lse) if lse is not None else None, *w, None)
+
+
+def test_fwd_v16_rejects_bad_arguments_before_launch():
+    d64 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=64, dtype="bf16")
+    d128 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=128, dtype="bf16")
+    df32 = aj.attn_jvp_mask_desc_build("block_causal", 4, 16, 1, head_dim=64, dtype="f32")
+    s64 = _shape(D=64, ins=(2 * 64 * 64, 64 * 64, 64), outs=(2 * 64 * 64, 64 * 64, 64))
+    assert _fwd_v16(s64, d64.handle, v16=None) == aj.AJ_EINVAL
+    assert _fwd_v16(s64, d64.handle, tv16=None) == aj.AJ_EINVAL
+    assert _fwd_v16(s64, d64.handle, v16=FAKE + 8) == aj.AJ_EINVAL             # misaligned copy buffer
+    assert _fwd_v16(_shape(), d128.handle) == aj.AJ_ENOTSUP                     # head_dim 128: no fp16 copies
+    s64f = _shape(D=64, idt=aj.AJ_F32, odt=aj.AJ_F32, ins=(2 * 64 * 64, 64 * 64, 64), outs=(2 * 64 * 64, 64 * 64, 64))
+    assert _fwd_v16(s64f, df32.handle) == aj.AJ_ENOTSUP                         # fp32 inputs
+    # the checks of attn_jvp_fwd apply as well
+    assert _fwd_v16(None, d64.handle) == aj.AJ_EINVAL
+    ptrs = [FAKE] * 8
+    ptrs[2] = None
+    assert _fwd_v16(s64, d64.handle, ptrs) == aj.AJ_EINVAL
+    assert _fwd_v16(s64, d64.handle, scale=float("nan")) == aj.AJ_EINVAL
+    assert _fwd_v16(s64, d128.handle) == aj.AJ_EMASK
+
+
 def test_fwd_without_gpu_reports_hip_error():
     import torch
     if torch.cuda.is_available():

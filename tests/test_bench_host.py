@@ -21,27 +21,34 @@ def test_more_than_one_gpu_is_refused():
 def test_kernel_names_follow_the_dispatch():
     assert bench.kernel_name("bf16", 128, False) == "attn_jvp_fwd_bf16_q16_kernel<128, false, false>"
     assert bench.kernel_name("bf16", 64, False, scale=0.125) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false, 4>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false, 4, false>"
     assert bench.kernel_name("bf16", 64, False, scale=0.1) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, false, 4>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, false, false, 4, false>"
+    # attn_jvp_fwd_v16: the conversion kernel, then the instance reading the fp16 copies
+    assert bench.kernel_name("bf16", 64, False, scale=0.125, v16=True) == \
+        "bf16_to_f16_kv_kernel<64> + attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, false, 4, true>"
+    assert bench.uses_v16("bf16", 64) and not bench.uses_v16("bf16", 128) and not bench.uses_v16("bf16", 64, "fwd")
     # the primal forward (and the KV step) at d = 128 runs 8-wave, 256-row tasks
     assert bench.kernel_name("bf16", 128, True, op="fwd") == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false, 8>"
+        "attn_jvp_fwd_bf16_q32_kernel<128, true, false, false, false, 8, false>"
     assert bench.kernel_name("bf16", 128, False, op="kv") == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 8>"
+        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 8, false>"
     assert bench.kernel_name("bf16", 64, False, op="fwd") == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4, false>"
     assert bench.kernel_name("bf16", 128, False, op="bwd") == \
         "attn_bwd_dq32_kernel<128, false> + attn_bwd_dkdv_kernel<128, false>"
     assert bench.kernel_name("bf16", 64, False, op="bwd") == \
         "attn_bwd_dq32_kernel<64, false> + attn_bwd_dkdv32_kernel<64, false>"
     # the primal-only query tiles of a tangent-free JVP keep 4-wave tasks
     assert bench.kernel_name("bf16", 128, False, tangent_free=True) == \
-        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 4> + " \
+        "attn_jvp_fwd_bf16_q32_kernel<128, false, false, false, false, 4, false> + " \
         "attn_jvp_fwd_bf16_q16_kernel<128, false, true>"
     assert bench.kernel_name("bf16", 64, False, tangent_free=True) == \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4> + " \
-        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true, 4>"
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4, false> + " \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true, 4, false>"
+    assert bench.kernel_name("bf16", 64, False, tangent_free=True, v16=True) == \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, false, false, false, 4, false> + bf16_to_f16_kv_kernel<64> + " \
+        "attn_jvp_fwd_bf16_q32_kernel<64, false, true, true, true, 4, true>"
     assert bench.kernel_name("f32", 64, True) == "attn_jvp_fwd_f32_kernel<64>"
 
 
@@ -50,8 +57,9 @@ def test_every_launched_kernel_has_a_code_hash():
     # instance bench.py can name must be among them
     for D, scale in ((128, None), (64, 0.125), (64, 0.1)):
         for tf in (False, True):
-            for name in bench.kernel_name("bf16", D, False, tangent_free=tf, scale=scale).split(" + "):
-                assert bench.kernel_isa_sha(name), name
+            for v16 in ((False, True) if D == 64 else (False,)):
+                for name in bench.kernel_name("bf16", D, False, tangent_free=tf, scale=scale, v16=v16).split(" + "):
+                    assert bench.kernel_isa_sha(name), name
         for op in ("fwd", "kv"):
             assert bench.kernel_isa_sha(bench.kernel_name("bf16", D, False, op=op)), (D, op)
         for name in bench.kernel_name("bf16", D, False, op="bwd").split(" + "):
@@ -96,9 +104,12 @@ def test_traffic_records_match_the_kernel_code():
         with open(path) as f:
             rec = json.load(f)
         w = WORKLOADS[rec["workload"]]
-        assert rec["kernel"] == bench.kernel_name(w.dtype, w.head_dim, False, scale=w.scale), path
+        kname = bench.kernel_name(w.dtype, w.head_dim, False, scale=w.scale,
+                                  v16=bench.uses_v16(w.dtype, w.head_dim)).split(" + ")[-1]
+        assert rec["kernel"] == kname, path
         assert rec["kernel_isa"] == bench.kernel_isa_sha(rec["kernel"]), path
-        assert bench.measured_traffic(w.name) == rec["bytes_per_launch"] > 0, path
+        assert bench.measured_traffic(w.name, kname) == rec["bytes_per_launch"] > 0, path
+        assert bench.measured_traffic(w.name, "another_kernel<1>") is None
 
 
 def test_counter_profiles_name_the_kernel_code_that_builds():
