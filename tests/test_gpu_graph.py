@@ -1,8 +1,8 @@
 """The launch paths under HIP graph capture.
 
 The descriptor builders upload the tables to the GPU; after that attn_jvp_fwd
-(also with a tangent-free descriptor: two launches), attn_fwd, attn_fwd_kv and
-attn_bwd enqueue kernels only: no allocation, no memset, no host
+(also with a tangent-free descriptor: two launches), attn_jvp_fwd_v16 (the fp16
+copies, then the JVP), attn_fwd, attn_fwd_kv and attn_bwd enqueue kernels only: no allocation, no memset, no host
 synchronisation, from the very first call on.  They are captured into a graph on torch's capture stream and
 the graph is replayed several times, with eager work and synchronisation in
 between; every replay must reproduce the eager results bit for bit (the
@@ -166,3 +166,46 @@ def test_first_launch_of_a_fresh_descriptor_is_captured():
     o, lse = aj.attn_fwd(dev["q"], dev["k"], dev["v"], host_only, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, want_fwd[0]) and torch.equal(lse, want_fwd[1])
+
+
+def test_fp16_copy_path_replays_from_a_graph():
+    # attn_jvp_fwd_v16: the conversion kernel and the JVP kernel, both captured;
+    # the copy buffers are filled with NaN between replays
+    w = Workload("graph_v16", 2, 2, 64, "bf16", "block_causal", 6, 70, 3, seed=162)
+    dev = {n: t.cuda() for n, t in make_inputs(w).items()}
+    desc = aj.attn_jvp_mask_desc_build(w.mask_kind, w.num_frames, w.frame_tokens, w.frames_per_chunk,
+                                       head_dim=w.head_dim, dtype=w.dtype)
+    B, H, L, D = w.shape
+    out = (torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+           torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda"),
+           torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    v16 = tuple(torch.empty_like(dev[n], dtype=torch.float16) for n in ("v", "tv"))
+
+    def run():
+        aj.attn_jvp_fwd_v16(*(dev[n] for n in NAMES), desc, scale=w.scale, out=out, v16=v16)
+
+    run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in out + v16]
+    plain = aj.attn_jvp_fwd(*(dev[n] for n in NAMES), desc, scale=w.scale)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(out, plain)), "attn_jvp_fwd_v16 differs from attn_jvp_fwd"
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for t in out + v16:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out + v16:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(out + v16, want):
+            assert torch.equal(got, ref), f"replay {rep} differs from the eager result"
