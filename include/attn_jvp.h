@@ -266,8 +266,9 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
  * the JVP kernel then reads the copies.  Same operation as attn_jvp_fwd
  * ("Causal-rCM", App. B, Eqs. 42-45), same results bit for bit, fewer
  * instructions per key tile.  v16 and tv16 must not overlap each other or any
- * other argument; their contents after the call are the copies.  Two kernels
- * in stream order; allocates nothing.  Errors: those of attn_jvp_fwd;
+ * other argument; after the call they hold the copies, unless a tangent-free
+ * declaration leaves only primal-only query tiles (then no JVP kernel runs and
+ * they are not written).  Two kernels in stream order; allocates nothing.  Errors: those of attn_jvp_fwd;
  * AJ_EINVAL for a null or misaligned v16 / tv16; AJ_ENOTSUP unless
  * head_dim is 64 and in_dtype AJ_BF16. */
 int32_t attn_jvp_fwd_v16(const aj_shape* shape, const void* q, const void* k, const void* v, const void* tq,
