@@ -413,6 +413,12 @@ int32_t attn_jvp_fwd_v16(const aj_shape* s, const void* q, const void* k, const 
                          const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o,
                          void* to, float* lse, void* v16, void* tv16, void* stream) {
   if (!v16 || !tv16 || !aligned16(v16) || !aligned16(tv16)) return AJ_EINVAL;
+  // the copies are written before the kernels read the inputs: the obvious
+  // aliases are rejected (partial overlaps remain the caller's to avoid)
+  for (const void* x : {q, k, v, tq, tk, tv, static_cast<const void*>(o), static_cast<const void*>(to),
+                        static_cast<const void*>(lse)})
+    if (x == v16 || x == tv16) return AJ_EINVAL;
+  if (v16 == tv16) return AJ_EINVAL;
   if (s && (s->head_dim != 64 || s->in_dtype != AJ_BF16)) return AJ_ENOTSUP;  // before any device work
   return jvp_fwd(s, q, k, v, tq, tk, tv, mask, scale, o, to, lse, v16, tv16, stream);
 }

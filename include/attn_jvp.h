@@ -268,9 +268,10 @@ int32_t attn_jvp_fwd(const aj_shape* shape, const void* q, const void* k, const 
  * instructions per key tile.  v16 and tv16 must not overlap each other or any
  * other argument; after the call they hold the copies, unless a tangent-free
  * declaration leaves only primal-only query tiles (then no JVP kernel runs and
- * they are not written).  Two kernels in stream order; allocates nothing.  Errors: those of attn_jvp_fwd;
- * AJ_EINVAL for a null or misaligned v16 / tv16; AJ_ENOTSUP unless
- * head_dim is 64 and in_dtype AJ_BF16. */
+ * they are not written).  Two kernels in stream order; allocates nothing.
+ * Errors: those of attn_jvp_fwd; AJ_EINVAL for a null or misaligned v16 /
+ * tv16, or one equal to another pointer argument; AJ_ENOTSUP unless head_dim
+ * is 64 and in_dtype AJ_BF16. */
 int32_t attn_jvp_fwd_v16(const aj_shape* shape, const void* q, const void* k, const void* v, const void* tq,
                          const void* tk, const void* tv, const aj_mask_desc* mask, float scale, void* o, void* to,
                          float* lse, void* v16, void* tv16, void* stream);

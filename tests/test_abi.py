@@ -186,6 +186,8 @@ def test_fwd_v16_rejects_bad_arguments_before_launch():
     assert _fwd_v16(s64, d64.handle, v16=None) == aj.AJ_EINVAL
     assert _fwd_v16(s64, d64.handle, tv16=None) == aj.AJ_EINVAL
     assert _fwd_v16(s64, d64.handle, v16=FAKE + 8) == aj.AJ_EINVAL             # misaligned copy buffer
+    assert _fwd_v16(s64, d64.handle, v16=FAKE) == aj.AJ_EINVAL                  # the copy buffer is an input
+    assert _fwd_v16(s64, d64.handle, v16=FAKE + 4096, tv16=FAKE + 4096) == aj.AJ_EINVAL  # one buffer for both
     assert _fwd_v16(_shape(), d128.handle) == aj.AJ_ENOTSUP                     # head_dim 128: no fp16 copies
     s64f = _shape(D=64, idt=aj.AJ_F32, odt=aj.AJ_F32, ins=(2 * 64 * 64, 64 * 64, 64), outs=(2 * 64 * 64, 64 * 64, 64))
     assert _fwd_v16(s64f, df32.handle) == aj.AJ_ENOTSUP                         # fp32 inputs
